@@ -1,0 +1,221 @@
+"""Python binding of libdpsgd.so, the C ABI of include/dpsgd.h (the DP-SGD private-gradient step:
+ghost per-record norms, clipping, clipped sum, Gaussian noise) on one MI355X GPU.
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch is used for device memory (tensor data pointers) and the current stream.  Importing this
+package fails loudly if the library has not been built (see __graft_entry__.build()).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdpsgd.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_NONFINITE = -3
+ERR_HIP = -4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+PATH_AUTO, PATH_GRAM, PATH_DIRECT = 0, 1, 2
+SUM_AUTO, SUM_GEMM, SUM_STORED = 0, 1, 2
+
+ACCUMULATE = 1
+NO_NOISE = 2
+
+EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
+           "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_norms", "dpsgd_clip",
+           "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_step", "dpsgd_status", "dpsgd_layer_norm2",
+           "dpsgd_philox_raw", "dpsgd_error_string", "dpsgd_last_error")
+
+
+class DpsgdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class LayerShape(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64)]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("layers", ctypes.POINTER(LayerShape)),
+                ("dtype", ctypes.c_int32), ("max_records", ctypes.c_int64),
+                ("tokens", ctypes.c_int64), ("path_policy", ctypes.c_int32),
+                ("sum_policy", ctypes.c_int32)]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [("n_records", ctypes.c_int64), ("A", ctypes.POINTER(ctypes.c_void_p)),
+                ("G", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.POINTER(ctypes.c_void_p)),
+                ("ws", ctypes.c_void_p), ("C", ctypes.c_double), ("sigma", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64), ("flags", ctypes.c_uint32),
+                ("norms_out", ctypes.c_void_p), ("clip_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load libdpsgd.so (raises if it is missing: there is no fallback implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U32, U64, D = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                ctypes.c_uint64, ctypes.c_double)
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    sigs = {
+        "dpsgd_plan_create": (ctypes.c_int, [ctypes.POINTER(PlanDesc), ctypes.POINTER(P),
+                                             ctypes.POINTER(ctypes.c_size_t)]),
+        "dpsgd_plan_destroy": (None, [P]),
+        "dpsgd_plan_layer_info": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "dpsgd_plan_num_params": (I64, [P]),
+        "dpsgd_ws_init": (ctypes.c_int, [P, P, P]),
+        "dpsgd_norms": (ctypes.c_int, [P, I64, I32, I32, PP, PP, P, P]),
+        "dpsgd_clip": (ctypes.c_int, [P, I64, D, U32, P, P, P, P]),
+        "dpsgd_clipped_sum": (ctypes.c_int, [P, I64, I32, I32, PP, PP, P, PP, U32, P, P]),
+        "dpsgd_noise": (ctypes.c_int, [P, PP, D, D, U64, U64, P, P]),
+        "dpsgd_step": (ctypes.c_int, [P, ctypes.POINTER(StepArgs), P]),
+        "dpsgd_status": (ctypes.c_int, [P, P, P]),
+        "dpsgd_layer_norm2": (ctypes.c_int, [P, I64, I32, I32, P, P, P]),
+        "dpsgd_philox_raw": (ctypes.c_int, [U64, U64, U64, U64, P, P]),
+        "dpsgd_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "dpsgd_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> int:
+    if rc != OK:
+        lib = load()
+        raise DpsgdError(rc, f"{lib.dpsgd_error_string(rc).decode()}: "
+                             f"{lib.dpsgd_last_error().decode()}")
+    return rc
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _ptr_array(xs) -> Optional[ctypes.Array]:
+    if xs is None:
+        return None
+    return (ctypes.c_void_p * max(1, len(xs)))(*[_ptr(x) for x in xs])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """Host plan of dpsgd_plan_create: layer shapes, dtype, record capacity, tokens per record."""
+
+    def __init__(self, layers: Sequence[tuple], dtype: int, max_records: int, tokens: int,
+                 path_policy: int = PATH_AUTO, sum_policy: int = SUM_AUTO):
+        lib = load()
+        self._layers = (LayerShape * len(layers))(*[LayerShape(int(a), int(b)) for a, b in layers]) \
+            if len(layers) else None
+        desc = PlanDesc(len(layers), self._layers, dtype, max_records, tokens, path_policy,
+                        sum_policy)
+        h = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        _check(lib.dpsgd_plan_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws)))
+        self.handle = h
+        self.ws_bytes = ws.value
+        self.layers = [tuple(x) for x in layers]
+        self.dtype = dtype
+        self.max_records = max_records
+        self.tokens = tokens
+        self.n_params = lib.dpsgd_plan_num_params(h)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.dpsgd_plan_destroy(self.handle)
+            self.handle = None
+
+    def layer_info(self, layer: int):
+        p, s = ctypes.c_int32(), ctypes.c_int32()
+        _check(load().dpsgd_plan_layer_info(self.handle, layer, ctypes.byref(p), ctypes.byref(s)))
+        return p.value, s.value
+
+    def workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+
+def ws_init(plan: Plan, ws, stream=None):
+    _check(load().dpsgd_ws_init(plan.handle, _ptr(ws), _stream(stream)))
+
+
+def norms(plan: Plan, n_records: int, l0: int, l1: int, A, G, ws, stream=None):
+    _check(load().dpsgd_norms(plan.handle, n_records, l0, l1, _ptr_array(A), _ptr_array(G),
+                              _ptr(ws), _stream(stream)))
+
+
+def clip(plan: Plan, n_records: int, C: float, ws, flags: int = 0, norms_out=None, clip_out=None,
+         stream=None):
+    _check(load().dpsgd_clip(plan.handle, n_records, C, flags, _ptr(ws), _ptr(norms_out),
+                             _ptr(clip_out), _stream(stream)))
+
+
+def clipped_sum(plan: Plan, n_records: int, l0: int, l1: int, A, G, clip_factors, out, ws,
+                flags: int = 0, stream=None):
+    _check(load().dpsgd_clipped_sum(plan.handle, n_records, l0, l1, _ptr_array(A), _ptr_array(G),
+                                    _ptr(clip_factors), _ptr_array(out), flags, _ptr(ws),
+                                    _stream(stream)))
+
+
+def noise(plan: Plan, out, C: float, sigma: float, seed: int, step: int, ws=None, stream=None):
+    _check(load().dpsgd_noise(plan.handle, _ptr_array(out), C, sigma, seed, step, _ptr(ws),
+                              _stream(stream)))
+
+
+def step(plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int, step_idx: int,
+         n_records: Optional[int] = None, flags: int = 0, norms_out=None, clip_out=None,
+         stream=None):
+    n = plan.max_records if n_records is None else n_records
+    a_arr, g_arr, o_arr = _ptr_array(A), _ptr_array(G), _ptr_array(out)
+    args = StepArgs(n, a_arr, g_arr, o_arr, _ptr(ws), C, sigma, seed, step_idx, flags,
+                    _ptr(norms_out), _ptr(clip_out))
+    _check(load().dpsgd_step(plan.handle, ctypes.byref(args), _stream(stream)))
+
+
+def status(plan: Plan, ws, stream=None) -> int:
+    """Synchronise the stream and return OK or ERR_NONFINITE."""
+    rc = load().dpsgd_status(plan.handle, _ptr(ws), _stream(stream))
+    if rc not in (OK, ERR_NONFINITE):
+        _check(rc)
+    return rc
+
+
+def layer_norm2(plan: Plan, n_records: int, l0: int, l1: int, ws, out, stream=None):
+    _check(load().dpsgd_layer_norm2(plan.handle, n_records, l0, l1, _ptr(ws), _ptr(out),
+                                    _stream(stream)))
+
+
+def philox_raw(seed: int, step: int, first_block: int, n_blocks: int, out, stream=None):
+    _check(load().dpsgd_philox_raw(seed, step, first_block, n_blocks, _ptr(out), _stream(stream)))

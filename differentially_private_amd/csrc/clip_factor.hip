@@ -1,0 +1,73 @@
+// clip_factor: one joint norm per record over all layers, then the clip factor
+//   n_i = sqrt(sum of the record's partial squared norms),
+//   c_i = 1 if n_i <= C (a zero gradient is left unchanged), else C / n_i
+// ("Privacy-Preserving Machine Learning", DP-SGD phase 3; the DP-SGD exhibit
+// card's g / max(1, ||g||/C) is the same factor).  One wavefront per record:
+// the lanes stride over the record's partials in a fixed order and a fixed
+// shuffle butterfly combines them (in fp64), so n_i and c_i depend only on the
+// record's own partials.  A single workgroup also resolves the status word
+// (nonfinite norm) without inter-block synchronisation.
+#include "device_common.h"
+#include "internal.h"
+
+namespace dpsgd {
+
+__global__ __launch_bounds__(1024) void k_clip(ClipArgs a) {
+    __shared__ uint32_t bad;
+    if (threadIdx.x == 0) bad = 0u;
+    __syncthreads();
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
+    for (int64_t rec = w; rec < a.n_rec; rec += nw) {
+        const float* p = a.parts + rec * a.parts_stride;
+        double s = 0.0;
+        for (int64_t k = lane; k < a.n_parts; k += 64) s += (double)p[k];
+        s = wave_sum_d(s);
+        if (lane == 0) {
+            const double n = sqrt(s);
+            const double cf = (n <= a.C) ? 1.0 : a.C / n;
+            if (!isfinite(s)) atomicOr(&bad, 1u);
+            a.n_ws[rec] = (float)n;
+            a.c_ws[rec] = (float)cf;
+            if (a.n_user) a.n_user[rec] = (float)n;
+            if (a.c_user) a.c_user[rec] = (float)cf;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *a.status = a.accumulate ? (*a.status | bad) : bad;
+}
+
+__global__ void k_status_clear(uint32_t* status) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *status = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_layer_norm2(LayerNormArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= a.n_rec * a.n_layers) return;
+    const int l = (int)(idx / a.n_rec);
+    const int64_t rec = idx - (int64_t)l * a.n_rec;
+    const float* p = a.parts + rec * a.parts_stride + a.part_off[l];
+    double s = 0.0;
+    for (int k = 0; k < a.n_part[l]; ++k) s += (double)p[k];
+    a.out[idx] = (float)s;
+}
+
+hipError_t launch_clip(const ClipArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_clip, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_status_clear(uint32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(k_status_clear, dim3(1), dim3(64), 0, s, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_norm2(const LayerNormArgs& a, hipStream_t s) {
+    const int64_t n = a.n_rec * a.n_layers;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_layer_norm2, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dpsgd

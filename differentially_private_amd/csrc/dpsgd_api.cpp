@@ -1,0 +1,637 @@
+// Host side of the C ABI in include/dpsgd.h: plan construction (path choice per
+// layer, workspace layout), argument validation (every argument error is
+// returned before anything is enqueued), and launch sequencing of the kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dpsgd.h"
+#include "internal.h"
+
+using namespace dpsgd;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return DPSGD_ERR_HIP;
+}
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    __int128 p = (__int128)a * (__int128)b;
+    if (p > (__int128)INT64_MAX / 4) return false;  // leave room for byte sizes
+    *out = (int64_t)p;
+    return true;
+}
+
+struct Tiles {
+    int x_is_in;
+    int64_t dX, dY;
+    int mb;
+    int tiles_x, tiles_y, wg_x;
+};
+
+Tiles direct_tiles(int64_t d_in, int64_t d_out) {
+    Tiles t;
+    t.x_is_in = d_in >= d_out ? 1 : 0;
+    t.dX = t.x_is_in ? d_in : d_out;
+    t.dY = t.x_is_in ? d_out : d_in;
+    t.mb = t.dY <= 16 ? 1 : 2;
+    t.tiles_x = (int)((t.dX + 127) / 128);
+    t.tiles_y = (int)((t.dY + 16 * t.mb - 1) / (16 * t.mb));
+    t.wg_x = (t.tiles_x + 3) / 4;
+    return t;
+}
+
+}  // namespace
+
+struct LayerPlan {
+    int64_t d_in, d_out, n_params, param_off;
+    int path;      // DPSGD_PATH_GRAM / DPSGD_PATH_DIRECT
+    int sum_mode;  // DPSGD_SUM_GEMM / DPSGD_SUM_STORED
+    Tiles tiles;   // direct decomposition (norm on the direct path, and the GEMM sum)
+    int nb, n_pairs;
+    int64_t n_parts, part_off;
+    int64_t stored_off;  // bytes into ws (STORED)
+    int64_t split_off;   // bytes into ws (GEMM with splits)
+};
+
+struct dpsgd_plan {
+    std::vector<LayerPlan> layers;
+    int dtype;
+    int64_t B, T;
+    int64_t parts_total;
+    int64_t n_params;
+    int n_splits_max;
+    int64_t status_off, parts_off, n_off, c_off;
+    int64_t ws_bytes;
+};
+
+namespace {
+
+int elem_size(int dtype) { return dtype == DPSGD_DTYPE_F32 ? 4 : 2; }
+
+bool ptr_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float* ws_f(void* ws, int64_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
+uint32_t* ws_status(void* ws, const dpsgd_plan* p) {
+    return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p->status_off);
+}
+
+int check_plan(const dpsgd_plan* p) {
+    if (!p) return fail(DPSGD_ERR_INVALID_ARG, "plan is NULL");
+    return DPSGD_OK;
+}
+
+int check_ws(const void* ws) {
+    if (!ws) return fail(DPSGD_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(DPSGD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    return DPSGD_OK;
+}
+
+int check_records(const dpsgd_plan* p, int64_t n) {
+    if (n < 0 || n > p->B)
+        return fail(DPSGD_ERR_INVALID_ARG, "n_records outside [0, max_records]");
+    return DPSGD_OK;
+}
+
+int check_range(const dpsgd_plan* p, int32_t l0, int32_t l1) {
+    if (l0 < 0 || l1 > (int32_t)p->layers.size() || l0 > l1)
+        return fail(DPSGD_ERR_INVALID_ARG, "layer range outside [0, n_layers]");
+    return DPSGD_OK;
+}
+
+int check_c_sigma(double C, double sigma, bool need_sigma) {
+    if (!std::isfinite(C) || !(C > 0.0)) return fail(DPSGD_ERR_INVALID_ARG, "C must be finite and > 0");
+    if (need_sigma && (!std::isfinite(sigma) || sigma < 0.0))
+        return fail(DPSGD_ERR_INVALID_ARG, "sigma must be finite and >= 0");
+    return DPSGD_OK;
+}
+
+// ---- phase implementations (arguments already validated) ----
+
+int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const* A,
+             const void* const* G, void* ws, hipStream_t s) {
+    if (n_rec == 0 || l0 == l1) return DPSGD_OK;
+    float* parts = ws_f(ws, p->parts_off);
+    const int es = elem_size(p->dtype);
+    // direct layers, grouped by (MB, store); Gram layers in their own launches
+    for (int mb = 1; mb <= 2; ++mb) {
+        for (int store = 0; store <= 1; ++store) {
+            DirectArgs a;
+            std::memset(&a, 0, sizeof(a));
+            a.T = p->T;
+            a.n_rec = n_rec;
+            a.parts_stride = p->parts_total;
+            a.parts = parts;
+            for (int l = l0; l < l1; ++l) {
+                const LayerPlan& lp = p->layers[l];
+                if (lp.path != DPSGD_PATH_DIRECT || lp.tiles.mb != mb ||
+                    (lp.sum_mode == DPSGD_SUM_STORED) != (store == 1))
+                    continue;
+                DirectLayer& d = a.L[a.n_layers];
+                const void* a_ptr = A[l - l0];
+                const void* g_ptr = G[l - l0];
+                d.X = lp.tiles.x_is_in ? a_ptr : g_ptr;
+                d.Y = lp.tiles.x_is_in ? g_ptr : a_ptr;
+                d.P = store ? ws_f(ws, lp.stored_off) : nullptr;
+                d.dX = (int32_t)lp.tiles.dX;
+                d.dY = (int32_t)lp.tiles.dY;
+                d.x_is_in = lp.tiles.x_is_in;
+                d.tiles_x = lp.tiles.tiles_x;
+                d.tiles_y = lp.tiles.tiles_y;
+                d.wg_x = lp.tiles.wg_x;
+                d.part_off = (int32_t)lp.part_off;
+                d.vec_x = ptr_aligned16(d.X) && ((lp.tiles.dX * es) % 16 == 0);
+                d.d_out = lp.d_out;
+                d.split_stride = 0;
+                if (++a.n_layers == kMaxLaunchLayers) {
+                    hipError_t e = launch_norm_direct(a, p->dtype, mb, store != 0, s);
+                    if (e != hipSuccess) return hip_fail(e, "ghost_norm (direct) launch");
+                    a.n_layers = 0;
+                }
+            }
+            if (a.n_layers) {
+                hipError_t e = launch_norm_direct(a, p->dtype, mb, store != 0, s);
+                if (e != hipSuccess) return hip_fail(e, "ghost_norm (direct) launch");
+            }
+        }
+    }
+    // Gram layers: grouped by identical block counts (all share T, so one group)
+    GramArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.T = p->T;
+    g.n_rec = n_rec;
+    g.parts_stride = p->parts_total;
+    g.parts = parts;
+    g.nb = (int32_t)((p->T + 63) / 64);
+    g.n_pairs = g.nb * (g.nb + 1) / 2;
+    for (int l = l0; l < l1; ++l) {
+        const LayerPlan& lp = p->layers[l];
+        if (lp.path != DPSGD_PATH_GRAM) continue;
+        GramLayer& d = g.L[g.n_layers];
+        d.A = A[l - l0];
+        d.G = G[l - l0];
+        d.d_in = (int32_t)lp.d_in;
+        d.d_out = (int32_t)lp.d_out;
+        d.part_off = (int32_t)lp.part_off;
+        d.vec_a = ptr_aligned16(d.A) && ((lp.d_in * es) % 16 == 0);
+        d.vec_g = ptr_aligned16(d.G) && ((lp.d_out * es) % 16 == 0);
+        if (++g.n_layers == kMaxLaunchLayers) {
+            hipError_t e = launch_norm_gram(g, p->dtype, s);
+            if (e != hipSuccess) return hip_fail(e, "ghost_norm (Gram) launch");
+            g.n_layers = 0;
+        }
+    }
+    if (g.n_layers) {
+        hipError_t e = launch_norm_gram(g, p->dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "ghost_norm (Gram) launch");
+    }
+    return DPSGD_OK;
+}
+
+int do_clip(const dpsgd_plan* p, int64_t n_rec, double C, uint32_t flags, void* ws,
+            float* n_user, float* c_user, hipStream_t s) {
+    ClipArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.parts = ws_f(ws, p->parts_off);
+    a.parts_stride = p->parts_total;
+    a.n_parts = p->parts_total;
+    a.n_rec = n_rec;
+    a.C = C;
+    a.n_ws = ws_f(ws, p->n_off);
+    a.c_ws = ws_f(ws, p->c_off);
+    a.n_user = n_user;
+    a.c_user = c_user;
+    a.status = ws_status(ws, p);
+    a.accumulate = (flags & DPSGD_ACCUMULATE) ? 1 : 0;
+    hipError_t e = launch_clip(a, s);
+    if (e != hipSuccess) return hip_fail(e, "clip_factor launch");
+    return DPSGD_OK;
+}
+
+int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const* A,
+           const void* const* G, const float* clip, float* const* out, uint32_t flags, void* ws,
+           hipStream_t s) {
+    if (l0 == l1) return DPSGD_OK;
+    const bool acc = (flags & DPSGD_ACCUMULATE) != 0;
+    const uint32_t* status = ws_status(ws, p);
+    if (!clip) clip = ws_f(ws, p->c_off);
+    const int es = elem_size(p->dtype);
+
+    // split count for this call
+    int ns = 1;
+    int64_t rps = n_rec;
+    if (n_rec > 0) {
+        ns = (int)std::min<int64_t>(p->n_splits_max, n_rec);
+        rps = (n_rec + ns - 1) / ns;
+        ns = (int)((n_rec + rps - 1) / rps);
+    }
+
+    // 1) STORED layers (and every layer when n_rec == 0): weighted reduce over records
+    {
+        ReduceArgs r;
+        std::memset(&r, 0, sizeof(r));
+        r.accumulate = acc;
+        r.n_src = n_rec;
+        r.clip = clip;
+        r.status = status;
+        auto flush = [&]() -> int {
+            if (!r.n_layers) return DPSGD_OK;
+            hipError_t e = launch_reduce(r, true, s);
+            if (e != hipSuccess) return hip_fail(e, "clipped_sum (stored) launch");
+            r.n_layers = 0;
+            r.max_n4 = 0;
+            return DPSGD_OK;
+        };
+        for (int l = l0; l < l1; ++l) {
+            const LayerPlan& lp = p->layers[l];
+            if (n_rec > 0 && lp.sum_mode != DPSGD_SUM_STORED) continue;
+            ReduceLayer& d = r.L[r.n_layers];
+            d.src = (lp.sum_mode == DPSGD_SUM_STORED) ? ws_f(ws, lp.stored_off) : nullptr;
+            d.out = out[l - l0];
+            d.n = lp.n_params;
+            r.max_n4 = std::max<int64_t>(r.max_n4, (lp.n_params + 3) / 4);
+            if (++r.n_layers == kMaxLaunchLayers) {
+                int rc = flush();
+                if (rc) return rc;
+            }
+        }
+        int rc = flush();
+        if (rc) return rc;
+    }
+    if (n_rec == 0) return DPSGD_OK;
+
+    // 2) GEMM layers: tile-engine sum, split over records, then a fixed-order reduce
+    for (int mb = 1; mb <= 2; ++mb) {
+        DirectArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.T = p->T;
+        a.n_rec = n_rec;
+        a.clip = clip;
+        a.rec_per_split = rps;
+        a.status = status;
+        a.accumulate = acc;
+        ReduceArgs r;
+        std::memset(&r, 0, sizeof(r));
+        r.accumulate = acc;
+        r.n_src = ns;
+        r.status = status;
+        auto flush = [&]() -> int {
+            if (!a.n_layers) return DPSGD_OK;
+            hipError_t e = launch_sum_direct(a, p->dtype, mb, ns, s);
+            if (e != hipSuccess) return hip_fail(e, "clipped_sum (GEMM) launch");
+            if (ns > 1) {
+                e = launch_reduce(r, false, s);
+                if (e != hipSuccess) return hip_fail(e, "clipped_sum (split reduce) launch");
+            }
+            a.n_layers = 0;
+            r.n_layers = 0;
+            r.max_n4 = 0;
+            return DPSGD_OK;
+        };
+        for (int l = l0; l < l1; ++l) {
+            const LayerPlan& lp = p->layers[l];
+            if (lp.sum_mode != DPSGD_SUM_GEMM || lp.tiles.mb != mb) continue;
+            DirectLayer& d = a.L[a.n_layers];
+            const void* a_ptr = A[l - l0];
+            const void* g_ptr = G[l - l0];
+            d.X = lp.tiles.x_is_in ? a_ptr : g_ptr;
+            d.Y = lp.tiles.x_is_in ? g_ptr : a_ptr;
+            d.dX = (int32_t)lp.tiles.dX;
+            d.dY = (int32_t)lp.tiles.dY;
+            d.x_is_in = lp.tiles.x_is_in;
+            d.tiles_x = lp.tiles.tiles_x;
+            d.tiles_y = lp.tiles.tiles_y;
+            d.wg_x = lp.tiles.wg_x;
+            d.vec_x = ptr_aligned16(d.X) && ((lp.tiles.dX * es) % 16 == 0);
+            d.d_out = lp.d_out;
+            if (ns > 1) {
+                d.P = ws_f(ws, lp.split_off);
+                d.split_stride = lp.n_params;
+                ReduceLayer& rl = r.L[r.n_layers++];
+                rl.src = d.P;
+                rl.out = out[l - l0];
+                rl.n = lp.n_params;
+                r.max_n4 = std::max<int64_t>(r.max_n4, (lp.n_params + 3) / 4);
+            } else {
+                d.P = out[l - l0];
+                d.split_stride = 0;
+            }
+            if (++a.n_layers == kMaxLaunchLayers) {
+                int rc = flush();
+                if (rc) return rc;
+            }
+        }
+        int rc = flush();
+        if (rc) return rc;
+    }
+    return DPSGD_OK;
+}
+
+int do_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, uint64_t seed,
+             uint64_t step, const void* ws, hipStream_t s) {
+    const int L = (int)p->layers.size();
+    NoiseArgs a;
+    for (int l0 = 0; l0 < L; l0 += kNoiseMaxLayers) {
+        const int l1 = std::min(L, l0 + kNoiseMaxLayers);
+        std::memset(&a, 0, sizeof(a));
+        a.n_layers = l1 - l0;
+        a.seed = seed;
+        a.step = step;
+        a.scale = (float)(sigma * C);
+        a.status = ws ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + p->status_off) : nullptr;
+        for (int l = l0; l < l1; ++l) {
+            a.out[l - l0] = out[l];
+            a.off[l - l0] = p->layers[l].param_off;
+        }
+        a.off[l1 - l0] = p->layers[l1 - 1].param_off + p->layers[l1 - 1].n_params;
+        hipError_t e = launch_noise(a, s);
+        if (e != hipSuccess) return hip_fail(e, "noise launch");
+    }
+    return DPSGD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_bytes) {
+    if (!d || !out || !ws_bytes) return fail(DPSGD_ERR_INVALID_ARG, "null argument");
+    *out = nullptr;
+    if (d->n_layers < 1 || !d->layers) return fail(DPSGD_ERR_INVALID_ARG, "n_layers < 1 or layers NULL");
+    if (d->dtype != DPSGD_DTYPE_F32 && d->dtype != DPSGD_DTYPE_BF16)
+        return fail(DPSGD_ERR_UNSUPPORTED, "dtype must be DPSGD_DTYPE_F32 or DPSGD_DTYPE_BF16");
+    if (d->path_policy < DPSGD_PATH_AUTO || d->path_policy > DPSGD_PATH_DIRECT)
+        return fail(DPSGD_ERR_UNSUPPORTED, "unknown path_policy");
+    if (d->sum_policy < DPSGD_SUM_AUTO || d->sum_policy > DPSGD_SUM_STORED)
+        return fail(DPSGD_ERR_UNSUPPORTED, "unknown sum_policy");
+    if (d->max_records < 1 || d->max_records > 65535)
+        return fail(DPSGD_ERR_INVALID_ARG, "max_records must be in [1, 65535]");
+    if (d->tokens < 1) return fail(DPSGD_ERR_INVALID_ARG, "tokens (T) must be >= 1");
+    const int es = elem_size(d->dtype);
+
+    dpsgd_plan* p = new (std::nothrow) dpsgd_plan();
+    if (!p) return fail(DPSGD_ERR_INVALID_ARG, "out of host memory");
+    p->dtype = d->dtype;
+    p->B = d->max_records;
+    p->T = d->tokens;
+    int64_t param_off = 0, part_off = 0;
+    for (int l = 0; l < d->n_layers; ++l) {
+        const int64_t di = d->layers[l].d_in, dd = d->layers[l].d_out;
+        if (di < 1 || dd < 1 || di > (1 << 30) || dd > (1 << 30)) {
+            delete p;
+            return fail(DPSGD_ERR_INVALID_ARG, "layer dimensions must be in [1, 2^30]");
+        }
+        int64_t np_, rows, in_bytes, tmp;
+        if (!mul_ok(di, dd, &np_) || !mul_ok(p->B, p->T, &rows) || !mul_ok(rows, di + dd, &tmp) ||
+            !mul_ok(tmp, es, &in_bytes) || !mul_ok(np_, p->B * 4, &tmp)) {
+            delete p;
+            return fail(DPSGD_ERR_INVALID_ARG, "sizes overflow");
+        }
+        LayerPlan lp;
+        std::memset(&lp, 0, sizeof(lp));
+        lp.d_in = di;
+        lp.d_out = dd;
+        lp.n_params = np_;
+        lp.param_off = param_off;
+        param_off += np_;
+        if (d->path_policy == DPSGD_PATH_AUTO) {
+            const __int128 t2 = (__int128)p->T * p->T;
+            lp.path = t2 < (__int128)di * dd ? DPSGD_PATH_GRAM : DPSGD_PATH_DIRECT;
+        } else {
+            lp.path = d->path_policy;
+        }
+        lp.tiles = direct_tiles(di, dd);
+        if (lp.path == DPSGD_PATH_GRAM) {
+            lp.nb = (int)((p->T + 63) / 64);
+            lp.n_pairs = lp.nb * (lp.nb + 1) / 2;
+            lp.n_parts = lp.n_pairs;
+            lp.sum_mode = DPSGD_SUM_GEMM;
+        } else {
+            lp.n_parts = (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
+            if (d->sum_policy == DPSGD_SUM_AUTO) {
+                // keep the per-record gradient blocks when writing + re-reading them (8 bytes
+                // per parameter) moves fewer bytes than re-reading the record's A and G rows
+                const __int128 stored = (__int128)8 * np_;
+                const __int128 reread = (__int128)p->T * (di + dd) * es;
+                lp.sum_mode = stored < reread ? DPSGD_SUM_STORED : DPSGD_SUM_GEMM;
+            } else {
+                lp.sum_mode = d->sum_policy;
+            }
+        }
+        lp.part_off = part_off;
+        part_off += lp.n_parts;
+        p->layers.push_back(lp);
+    }
+    p->parts_total = part_off;
+    p->n_params = param_off;
+    if (p->parts_total > INT32_MAX) {
+        delete p;
+        return fail(DPSGD_ERR_INVALID_ARG, "too many norm partials");
+    }
+
+    // split count of the GEMM clipped sum: aim for ~8192 wavefronts per launch
+    int64_t waves = 0;
+    for (const LayerPlan& lp : p->layers)
+        if (lp.sum_mode == DPSGD_SUM_GEMM) waves += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
+    int ns = 1;
+    if (waves > 0) ns = (int)std::min<int64_t>(std::min<int64_t>(p->B, 64), std::max<int64_t>(1, (8192 + waves - 1) / waves));
+    p->n_splits_max = ns;
+
+    // workspace layout
+    int64_t off = 0;
+    p->status_off = off;
+    off += kAlign;
+    p->parts_off = off;
+    off = align_up(off + p->B * p->parts_total * 4);
+    p->n_off = off;
+    off = align_up(off + p->B * 4);
+    p->c_off = off;
+    off = align_up(off + p->B * 4);
+    for (LayerPlan& lp : p->layers) {
+        if (lp.sum_mode == DPSGD_SUM_STORED) {
+            lp.stored_off = off;
+            off = align_up(off + p->B * lp.n_params * 4);
+        } else if (ns > 1) {
+            lp.split_off = off;
+            off = align_up(off + (int64_t)ns * lp.n_params * 4);
+        }
+    }
+    p->ws_bytes = off;
+    *ws_bytes = (size_t)off;
+    *out = p;
+    return DPSGD_OK;
+}
+
+void dpsgd_plan_destroy(dpsgd_plan* p) { delete p; }
+
+int dpsgd_plan_layer_info(const dpsgd_plan* p, int32_t layer, int32_t* path, int32_t* sum_mode) {
+    if (int rc = check_plan(p)) return rc;
+    if (layer < 0 || layer >= (int32_t)p->layers.size()) return fail(DPSGD_ERR_INVALID_ARG, "layer out of range");
+    if (path) *path = p->layers[layer].path;
+    if (sum_mode) *sum_mode = p->layers[layer].sum_mode;
+    return DPSGD_OK;
+}
+
+int64_t dpsgd_plan_num_params(const dpsgd_plan* p) { return p ? p->n_params : -1; }
+
+int dpsgd_ws_init(const dpsgd_plan* p, void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    hipError_t e = launch_status_clear(ws_status(ws, p), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "status clear launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_norms(const dpsgd_plan* p, int64_t n_rec, int32_t l0, int32_t l1, const void* const* A,
+                const void* const* G, void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_records(p, n_rec)) return rc;
+    if (int rc = check_range(p, l0, l1)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    if (l1 > l0 && (!A || !G)) return fail(DPSGD_ERR_INVALID_ARG, "A or G array is NULL");
+    for (int l = l0; l < l1 && n_rec > 0; ++l)
+        if (!A[l - l0] || !G[l - l0]) return fail(DPSGD_ERR_INVALID_ARG, "null A or G pointer");
+    return do_norms(p, n_rec, l0, l1, A, G, ws, (hipStream_t)stream);
+}
+
+int dpsgd_clip(const dpsgd_plan* p, int64_t n_rec, double C, uint32_t flags, void* ws,
+               float* norms_out, float* clip_out, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_records(p, n_rec)) return rc;
+    if (int rc = check_c_sigma(C, 0.0, false)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    if (flags & ~(DPSGD_ACCUMULATE | DPSGD_NO_NOISE)) return fail(DPSGD_ERR_INVALID_ARG, "unknown flags");
+    return do_clip(p, n_rec, C, flags, ws, norms_out, clip_out, (hipStream_t)stream);
+}
+
+int dpsgd_clipped_sum(const dpsgd_plan* p, int64_t n_rec, int32_t l0, int32_t l1,
+                      const void* const* A, const void* const* G, const float* clip,
+                      float* const* out, uint32_t flags, void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_records(p, n_rec)) return rc;
+    if (int rc = check_range(p, l0, l1)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    if (flags & ~(DPSGD_ACCUMULATE | DPSGD_NO_NOISE)) return fail(DPSGD_ERR_INVALID_ARG, "unknown flags");
+    if (l1 > l0 && !out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
+    for (int l = l0; l < l1; ++l) {
+        if (!out[l - l0]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
+        if (n_rec > 0 && p->layers[l].sum_mode == DPSGD_SUM_GEMM &&
+            (!A || !G || !A[l - l0] || !G[l - l0]))
+            return fail(DPSGD_ERR_INVALID_ARG, "null A or G pointer for a GEMM-sum layer");
+    }
+    return do_sum(p, n_rec, l0, l1, A, G, clip, out, flags, ws, (hipStream_t)stream);
+}
+
+int dpsgd_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, uint64_t seed,
+                uint64_t step, const void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_c_sigma(C, sigma, true)) return rc;
+    if (ws && reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(DPSGD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (!out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
+    for (size_t l = 0; l < p->layers.size(); ++l)
+        if (!out[l]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
+    return do_noise(p, out, C, sigma, seed, step, ws, (hipStream_t)stream);
+}
+
+int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (!a) return fail(DPSGD_ERR_INVALID_ARG, "args is NULL");
+    if (int rc = check_records(p, a->n_records)) return rc;
+    if (int rc = check_c_sigma(a->C, a->sigma, true)) return rc;
+    if (int rc = check_ws(a->ws)) return rc;
+    if (a->flags & ~(DPSGD_ACCUMULATE | DPSGD_NO_NOISE)) return fail(DPSGD_ERR_INVALID_ARG, "unknown flags");
+    const int L = (int)p->layers.size();
+    if (!a->out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
+    if (a->n_records > 0 && (!a->A || !a->G)) return fail(DPSGD_ERR_INVALID_ARG, "A or G array is NULL");
+    for (int l = 0; l < L; ++l) {
+        if (!a->out[l]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
+        if (a->n_records > 0 && (!a->A[l] || !a->G[l])) return fail(DPSGD_ERR_INVALID_ARG, "null A or G pointer");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (int rc = do_norms(p, a->n_records, 0, L, a->A, a->G, a->ws, s)) return rc;
+    if (int rc = do_clip(p, a->n_records, a->C, a->flags, a->ws, a->norms_out, a->clip_out, s)) return rc;
+    if (int rc = do_sum(p, a->n_records, 0, L, a->A, a->G, nullptr, a->out, a->flags, a->ws, s)) return rc;
+    if (!(a->flags & DPSGD_NO_NOISE))
+        if (int rc = do_noise(p, a->out, a->C, a->sigma, a->seed, a->step, a->ws, s)) return rc;
+    return DPSGD_OK;
+}
+
+int dpsgd_status(const dpsgd_plan* p, const void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    uint32_t v = 0;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(&v, static_cast<const char*>(ws) + p->status_off, 4, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "status copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    return v ? DPSGD_ERR_NONFINITE : DPSGD_OK;
+}
+
+int dpsgd_layer_norm2(const dpsgd_plan* p, int64_t n_rec, int32_t l0, int32_t l1, const void* ws,
+                      float* out, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_records(p, n_rec)) return rc;
+    if (int rc = check_range(p, l0, l1)) return rc;
+    if (int rc = check_ws(ws)) return rc;
+    if (!out) return fail(DPSGD_ERR_INVALID_ARG, "out is NULL");
+    for (int b = l0; b < l1; b += kMaxLaunchLayers) {
+        const int e_ = std::min(l1, b + kMaxLaunchLayers);
+        LayerNormArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.parts = reinterpret_cast<const float*>(static_cast<const char*>(ws) + p->parts_off);
+        a.parts_stride = p->parts_total;
+        a.n_rec = n_rec;
+        a.n_layers = e_ - b;
+        for (int l = b; l < e_; ++l) {
+            a.part_off[l - b] = (int32_t)p->layers[l].part_off;
+            a.n_part[l - b] = (int32_t)p->layers[l].n_parts;
+        }
+        a.out = out + (int64_t)(b - l0) * n_rec;
+        hipError_t e = launch_layer_norm2(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "layer norm launch");
+    }
+    return DPSGD_OK;
+}
+
+int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_t n_blocks,
+                     uint32_t* dev_out, void* stream) {
+    if (n_blocks > 0 && !dev_out) return fail(DPSGD_ERR_INVALID_ARG, "dev_out is NULL");
+    if (n_blocks > (1ull << 40)) return fail(DPSGD_ERR_INVALID_ARG, "n_blocks too large");
+    if (first_block + n_blocks < first_block) return fail(DPSGD_ERR_INVALID_ARG, "block range wraps");
+    hipError_t e = launch_philox_raw(seed, step, first_block, n_blocks, dev_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "philox launch");
+    return DPSGD_OK;
+}
+
+const char* dpsgd_error_string(int code) {
+    switch (code) {
+        case DPSGD_OK: return "ok";
+        case DPSGD_ERR_INVALID_ARG: return "invalid argument";
+        case DPSGD_ERR_UNSUPPORTED: return "unsupported dtype or policy";
+        case DPSGD_ERR_NONFINITE: return "nonfinite per-record norm: clipped sum and noise skipped";
+        case DPSGD_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status code";
+    }
+}
+
+const char* dpsgd_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

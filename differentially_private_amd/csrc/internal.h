@@ -1,0 +1,131 @@
+// Internal interface between the host API (dpsgd_api.cpp) and the kernel
+// translation units.  Kernel-argument structs are passed by value, so every
+// per-layer pointer travels in the kernarg segment (no device-side tables).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpsgd {
+
+constexpr int kMaxLaunchLayers = 48;  // per-launch layer descriptors (kernarg <= 4 KB)
+constexpr int kNoiseMaxLayers = 64;
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+
+// Tile decomposition of one layer on the direct path.  X is the operand whose
+// columns are streamed 128 at a time (the larger of d_in / d_out), Y the other
+// one, whose columns form 16*MB-row MFMA blocks.
+struct DirectLayer {
+    const void* X;      // [n_rec, T, dX]
+    const void* Y;      // [n_rec, T, dY]
+    float* P;           // NORM+STORE: per-record gradient blocks [rec][d_in*d_out]; SUM: destination
+    int32_t dX, dY;
+    int32_t x_is_in;    // 1: X = A (d_in), Y = G (d_out); 0: X = G, Y = A
+    int32_t tiles_x;    // ceil(dX / 128)
+    int32_t tiles_y;    // ceil(dY / (16*MB))
+    int32_t wg_x;       // ceil(tiles_x / 4)
+    int32_t part_off;   // first norm partial of this layer
+    int32_t vec_x;      // X rows are 16-byte aligned (vector loads allowed)
+    int64_t d_out;      // for output addressing
+    int64_t split_stride;  // SUM: floats between split partial blocks (0 = write `P` directly)
+};
+
+struct DirectArgs {
+    DirectLayer L[kMaxLaunchLayers];
+    int32_t n_layers;
+    int32_t accumulate;        // SUM with direct write: out += tile
+    int64_t T;
+    int64_t n_rec;
+    int64_t parts_stride;      // partials per record (record-major partial array)
+    float* parts;
+    const float* clip;         // SUM: per-record factors
+    int64_t rec_per_split;     // SUM
+    const uint32_t* status;    // SUM: skip while nonzero
+};
+
+struct GramLayer {
+    const void* A;     // [n_rec, T, d_in]
+    const void* G;     // [n_rec, T, d_out]
+    int32_t d_in, d_out;
+    int32_t part_off;
+    int32_t vec_a, vec_g;
+    int32_t pad;
+};
+
+struct GramArgs {
+    GramLayer L[kMaxLaunchLayers];
+    int32_t n_layers;
+    int32_t nb;        // 64-row blocks of T
+    int32_t n_pairs;   // nb (nb + 1) / 2 upper-triangle block pairs
+    int32_t pad;
+    int64_t T;
+    int64_t n_rec;
+    int64_t parts_stride;
+    float* parts;
+};
+
+struct ClipArgs {
+    const float* parts;
+    int64_t parts_stride;
+    int64_t n_parts;
+    int64_t n_rec;
+    double C;
+    float* n_ws;
+    float* c_ws;
+    float* n_user;
+    float* c_user;
+    uint32_t* status;
+    int32_t accumulate;
+};
+
+struct ReduceLayer {
+    const float* src;   // SPLIT: [n_splits][n]; STORED: [n_rec][n]
+    float* out;         // [n]
+    int64_t n;          // elements (d_in * d_out)
+};
+
+struct ReduceArgs {
+    ReduceLayer L[kMaxLaunchLayers];
+    int32_t n_layers;
+    int32_t accumulate;
+    int64_t n_src;       // splits or records
+    const float* clip;   // STORED: weights per record; SPLIT: null
+    const uint32_t* status;
+    int64_t max_n4;      // max over layers of ceil(n / 4)
+};
+
+struct NoiseArgs {
+    float* out[kNoiseMaxLayers];
+    int64_t off[kNoiseMaxLayers + 1];  // flat offsets of the launch's layers, off[0] = first flat index
+    int32_t n_layers;
+    int32_t pad;
+    uint64_t seed, step;
+    float scale;                       // sigma * C
+    const uint32_t* status;
+};
+
+struct LayerNormArgs {
+    const float* parts;
+    int64_t parts_stride;
+    int64_t n_rec;
+    int32_t n_layers;
+    int32_t pad;
+    int32_t part_off[kMaxLaunchLayers];
+    int32_t n_part[kMaxLaunchLayers];
+    float* out;
+};
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s);
+hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s);
+hipError_t launch_clip(const ClipArgs& a, hipStream_t s);
+hipError_t launch_sum_direct(const DirectArgs& a, int dtype, int mb, int n_splits, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, bool weighted, hipStream_t s);
+hipError_t launch_noise(const NoiseArgs& a, hipStream_t s);
+hipError_t launch_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_t n_blocks,
+                             uint32_t* out, hipStream_t s);
+hipError_t launch_layer_norm2(const LayerNormArgs& a, hipStream_t s);
+hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
+
+}  // namespace dpsgd

@@ -1,0 +1,201 @@
+/*
+ * dpsgd.h -- C ABI of the DP-SGD private-gradient step on one AMD Instinct
+ * MI355X (gfx950) GPU.
+ *
+ * The step (Abadi et al. DP-SGD, restated in "Privacy-Preserving Machine
+ * Learning", section "Differentially private stochastic gradient descent",
+ * phases 2-4, and in "Sensitivity Inflation from Cross-Record Precision
+ * Routing in Private Quantized Fine-Tuning", Sec. 2, Eqs. 2-3):
+ *
+ *   for each record i of the batch and each trainable linear layer l, with the
+ *   layer's input activations A_l[i] (T x d_in) and output gradients
+ *   G_l[i] (T x d_out), the record's gradient is P_{i,l} = A_l[i]^T G_l[i]
+ *   (d_in x d_out, summed over the record's T tokens);
+ *   n_i   = || (P_{i,1}, ..., P_{i,L}) ||_2        one norm over all layers
+ *   c_i   = 1 if n_i <= C (also n_i = 0), else C / n_i
+ *   S_l   = sum_i c_i P_{i,l}                     the clipped sum
+ *   S~_l  = S_l + sigma * C * Z_l,  Z ~ N(0, I)    noise once per logical step
+ *
+ * n_i is computed without forming P_{i,l} ("ghost" norms): through the Gram
+ * identity sum_{t,s} (a_t . a_s)(g_t . g_s) when T^2 < d_in * d_out, else from
+ * tiles of P_{i,l} that never leave registers.  Z comes from Philox4x32-10
+ * (Salmon et al., SC'11) keyed by the 64-bit seed, counter = (flat element
+ * index / 4, step), and the Box-Muller transform; the library never divides
+ * by the batch size (that belongs to the optimizer step, phase 5).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers point to memory on the current HIP device; `stream` is a
+ *    hipStream_t (NULL = the default stream).  All launches are asynchronous on
+ *    `stream` unless stated otherwise.
+ *  - Host pointer arrays (A, G, out) are read during the call only.
+ *  - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *    allocates no device memory and keeps no device state.
+ *  - Argument errors are detected on the host before any launch and returned
+ *    as DPSGD_ERR_INVALID_ARG / DPSGD_ERR_UNSUPPORTED; nothing is enqueued then.
+ *    No C++ exception crosses this interface.  dpsgd_last_error() gives a
+ *    thread-local text for the last failure.
+ *  - Records: A_l is [n_records, T, d_in] and G_l is [n_records, T, d_out],
+ *    row-major, contiguous, in the plan's dtype.  A record owns its T rows in
+ *    every layer; padding tokens are zero rows of G.  Any loss normaliser is
+ *    already folded into G.
+ *  - Outputs out_l are [d_in, d_out] row-major float32 (the transpose of the
+ *    gradient of a weight stored d_out x d_in).
+ */
+#ifndef DPSGD_H
+#define DPSGD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define DPSGD_OK 0
+#define DPSGD_ERR_INVALID_ARG (-1) /* bad pointer, size, C, sigma, layer range, flags */
+#define DPSGD_ERR_UNSUPPORTED (-2) /* dtype or policy value not supported */
+#define DPSGD_ERR_NONFINITE (-3)   /* a record's norm was NaN/Inf: sums and noise were skipped */
+#define DPSGD_ERR_HIP (-4)         /* the HIP runtime reported an error (see dpsgd_last_error) */
+
+/* ---- element types of A and G ---- */
+#define DPSGD_DTYPE_F32 0
+#define DPSGD_DTYPE_BF16 1
+
+/* ---- per-layer norm path ---- */
+#define DPSGD_PATH_AUTO 0   /* Gram iff T^2 < d_in * d_out (a tie takes the direct path) */
+#define DPSGD_PATH_GRAM 1   /* force the Gram identity for every layer */
+#define DPSGD_PATH_DIRECT 2 /* force per-record gradient tiles for every layer */
+
+/* ---- clipped-sum strategy ---- */
+#define DPSGD_SUM_AUTO 0   /* STORED where it moves fewer HBM bytes, else GEMM */
+#define DPSGD_SUM_GEMM 1   /* S = A^T diag(c) G, re-reading A and G */
+#define DPSGD_SUM_STORED 2 /* direct-path layers keep each record's gradient block in the
+                              workspace during dpsgd_norms; the sum reads it back (Gram-path
+                              layers fall back to GEMM) */
+
+/* ---- flags ---- */
+#define DPSGD_ACCUMULATE 1u /* add into out (and OR into the status) instead of overwriting */
+#define DPSGD_NO_NOISE 2u   /* dpsgd_step: skip the noise phase */
+
+typedef struct dpsgd_layer_shape {
+    int64_t d_in;
+    int64_t d_out;
+} dpsgd_layer_shape;
+
+typedef struct dpsgd_plan_desc {
+    int32_t n_layers;                /* >= 1 */
+    const dpsgd_layer_shape* layers; /* n_layers shapes, in plan order (also the noise order) */
+    int32_t dtype;                   /* DPSGD_DTYPE_*: one type for all A and G */
+    int64_t max_records;             /* largest n_records of any call (>= 1) */
+    int64_t tokens;                  /* T, tokens per record (>= 1) */
+    int32_t path_policy;             /* DPSGD_PATH_* */
+    int32_t sum_policy;              /* DPSGD_SUM_* */
+} dpsgd_plan_desc;
+
+typedef struct dpsgd_plan dpsgd_plan; /* immutable host object */
+
+typedef struct dpsgd_step_args {
+    int64_t n_records;     /* 0 <= n_records <= max_records (0: empty batch, noise only) */
+    const void* const* A;  /* n_layers device pointers, A_l [n_records, T, d_in] */
+    const void* const* G;  /* n_layers device pointers, G_l [n_records, T, d_out] */
+    float* const* out;     /* n_layers device pointers, out_l [d_in, d_out] float32 */
+    void* ws;              /* device workspace of dpsgd_plan_create's ws_bytes (256-B aligned) */
+    double C;              /* clipping bound, finite and > 0 */
+    double sigma;          /* noise multiplier, finite and >= 0 */
+    uint64_t seed;         /* Philox key */
+    uint64_t step;         /* Philox counter words 2-3 (e.g. the logical step index) */
+    uint32_t flags;        /* DPSGD_ACCUMULATE | DPSGD_NO_NOISE */
+    float* norms_out;      /* optional device [n_records]: n_i */
+    float* clip_out;       /* optional device [n_records]: c_i */
+} dpsgd_step_args;
+
+/* Build a plan: validate shapes, choose the path of every layer and lay out
+ * the workspace.  Host only (no device call).  *ws_bytes receives the size of
+ * the device workspace every call with this plan needs.  Returns
+ * DPSGD_ERR_INVALID_ARG for a null pointer, n_layers < 1, a dimension < 1,
+ * max_records < 1, T < 1, or sizes whose products overflow 64 bits;
+ * DPSGD_ERR_UNSUPPORTED for an unknown dtype or policy. */
+int dpsgd_plan_create(const dpsgd_plan_desc* desc, dpsgd_plan** out, size_t* ws_bytes);
+
+/* Free a plan (NULL is ignored). */
+void dpsgd_plan_destroy(dpsgd_plan* plan);
+
+/* Path (DPSGD_PATH_GRAM / _DIRECT) and sum strategy (DPSGD_SUM_GEMM / _STORED)
+ * chosen for `layer`.  Host only. */
+int dpsgd_plan_layer_info(const dpsgd_plan* plan, int32_t layer, int32_t* path, int32_t* sum_mode);
+
+/* Total trainable parameters sum_l d_in * d_out (the flat noise index space). */
+int64_t dpsgd_plan_num_params(const dpsgd_plan* plan);
+
+/* Clear the workspace status word (a fill kernel, no memset node).  Needed only
+ * before a dpsgd_noise with a workspace that no dpsgd_clip has touched yet. */
+int dpsgd_ws_init(const dpsgd_plan* plan, void* ws, void* stream);
+
+/* Phase 1 ("Privacy-Preserving Machine Learning", DP-SGD phase 2, computed
+ * without per-record gradient tensors): per-record partial squared norms of
+ * layers [l0, l1) into the workspace.  A and G hold (l1 - l0) device pointers,
+ * entry k for layer l0 + k.  For layers whose sum strategy is STORED, each
+ * record's gradient block is also written to the workspace.  Calls over
+ * disjoint layer ranges may be issued in any order before dpsgd_clip
+ * (layer-chunk streaming). */
+int dpsgd_norms(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int32_t l1,
+                const void* const* A, const void* const* G, void* ws, void* stream);
+
+/* Phase 2 (DP-SGD phase 3, g * min(1, C/||g||)): n_i and c_i from the partials
+ * of all layers (fixed summation order: record i's results do not depend on the
+ * other records, their number or i's position).  Sets the status word to
+ * NONFINITE if some n_i is NaN/Inf (ORs into it with DPSGD_ACCUMULATE).
+ * norms_out / clip_out are optional device arrays of n_records floats. */
+int dpsgd_clip(const dpsgd_plan* plan, int64_t n_records, double C, uint32_t flags, void* ws,
+               float* norms_out, float* clip_out, void* stream);
+
+/* Phase 3 (DP-SGD phase 4, sum of the clipped gradients; Eq. 3 F(D)): for
+ * layers [l0, l1), out_l = sum_i c_i A_l[i]^T G_l[i] (or out_l += ... with
+ * DPSGD_ACCUMULATE).  `clip` is a device array of n_records factors, or NULL
+ * to use the factors of the last dpsgd_clip in `ws`.  For STORED layers the
+ * gradient blocks written by the last dpsgd_norms are used and A_l/G_l may be
+ * NULL.  Skipped on device (out untouched) while the status is NONFINITE. */
+int dpsgd_clipped_sum(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int32_t l1,
+                      const void* const* A, const void* const* G, const float* clip,
+                      float* const* out, uint32_t flags, void* ws, void* stream);
+
+/* Phase 4 (DP-SGD phase 4, N(0, sigma^2 C^2 I) added once): out_l[e] +=
+ * sigma * C * Z[off_l + e] over all layers (off_l = parameters of the layers
+ * before l).  Z is a pure function of (seed, step, flat index).  ws may be NULL
+ * (no status check); else the launch is skipped on device while the status is
+ * NONFINITE. */
+int dpsgd_noise(const dpsgd_plan* plan, float* const* out, double C, double sigma, uint64_t seed,
+                uint64_t step, const void* ws, void* stream);
+
+/* The whole step: dpsgd_norms(all layers) -> dpsgd_clip -> dpsgd_clipped_sum
+ * (all layers) -> dpsgd_noise unless DPSGD_NO_NOISE.  Virtual batching: call
+ * with DPSGD_NO_NOISE for every physical batch, DPSGD_ACCUMULATE for all but
+ * the first, then dpsgd_noise once. */
+int dpsgd_step(const dpsgd_plan* plan, const dpsgd_step_args* args, void* stream);
+
+/* Synchronise `stream` and read the status word: DPSGD_OK or
+ * DPSGD_ERR_NONFINITE (or DPSGD_ERR_HIP). */
+int dpsgd_status(const dpsgd_plan* plan, const void* ws, void* stream);
+
+/* Per-layer squared norms of layers [l0, l1) from the partials of the last
+ * dpsgd_norms: out[(l - l0) * n_records + i] = ||P_{i,l}||_F^2 (device). */
+int dpsgd_layer_norm2(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int32_t l1,
+                      const void* ws, float* out, void* stream);
+
+/* Raw Philox4x32-10 words of blocks first_block .. first_block + n_blocks - 1
+ * for key = seed and counter = (block, step): 4 * n_blocks uint32 at dev_out. */
+int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_t n_blocks,
+                     uint32_t* dev_out, void* stream);
+
+/* Static text for a status code. */
+const char* dpsgd_error_string(int code);
+
+/* Thread-local text describing the last failed call on this thread. */
+const char* dpsgd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPSGD_H */

@@ -65,23 +65,46 @@ void orc_record_grad(int dtype, const void* A_i, const void* G_i, int64_t T, int
 static size_t orc_esize(int dtype) { return dtype == ORC_F64 ? 8 : (dtype == ORC_F32 ? 4 : 2); }
 static int orc_dtype_ok(int dtype) { return dtype == ORC_F32 || dtype == ORC_BF16 || dtype == ORC_F64; }
 
+/* Row j of one record's gradient: row[k] = sum_t A_i[t][j] * G_i[t][k]. */
+static void orc_grad_row(int dtype, const void* A_i, const void* G_i, int64_t T, int64_t d_in,
+                         int64_t d_out, int64_t j, double* row) {
+    for (int64_t k = 0; k < d_out; ++k) row[k] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const double a = orc_elem(A_i, dtype, t * d_in + j);
+        for (int64_t k = 0; k < d_out; ++k) row[k] += a * orc_elem(G_i, dtype, t * d_out + k);
+    }
+}
+
 /* Squared Frobenius norm of every record's gradient of one layer:
- * norm2[i] = sum_{j,k} P_i[j,k]^2, for records i = 0..B-1 of A [B,T,d_in], G [B,T,d_out]. */
+ * norm2[i] = sum_{j,k} P_i[j,k]^2, for records i = 0..B-1 of A [B,T,d_in], G [B,T,d_out].
+ * Every row of every P_i is materialised (rows in parallel); each row's sum of squares is
+ * kept and the rows are added in ascending order. */
 int orc_layer_norm2(int dtype, const void* A, const void* G, int64_t B, int64_t T, int64_t d_in,
                     int64_t d_out, double* norm2) {
     if (!orc_dtype_ok(dtype)) return -1;
     const size_t es = orc_esize(dtype);
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < B; ++i) {
-        double* P = (double*)malloc(sizeof(double) * (size_t)(d_in * d_out));
-        const char* Ai = (const char*)A + (size_t)(i * T * d_in) * es;
-        const char* Gi = (const char*)G + (size_t)(i * T * d_out) * es;
-        orc_record_grad(dtype, Ai, Gi, T, d_in, d_out, P);
-        double s = 0.0;
-        for (int64_t x = 0; x < d_in * d_out; ++x) s += P[x] * P[x];
-        norm2[i] = s;
-        free(P);
+    double* rowsq = (double*)malloc(sizeof(double) * (size_t)(B * d_in));
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * (size_t)d_out);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t task = 0; task < B * d_in; ++task) {
+            const int64_t i = task / d_in, j = task % d_in;
+            const char* Ai = (const char*)A + (size_t)(i * T * d_in) * es;
+            const char* Gi = (const char*)G + (size_t)(i * T * d_out) * es;
+            orc_grad_row(dtype, Ai, Gi, T, d_in, d_out, j, row);
+            double s = 0.0;
+            for (int64_t k = 0; k < d_out; ++k) s += row[k] * row[k];
+            rowsq[task] = s;
+        }
+        free(row);
     }
+    for (int64_t i = 0; i < B; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < d_in; ++j) s += rowsq[i * d_in + j];
+        norm2[i] = s;
+    }
+    free(rowsq);
     return 0;
 }
 
@@ -101,38 +124,25 @@ void orc_clip(const double* norm2, int64_t B, double C, double* n_out, double* c
 }
 
 /* S[j*d_out + k] += sum_i c[i] * P_i[j,k], records in ascending order.
- * Each thread owns a band of rows j, so the per-entry order stays i = 0..B-1. */
+ * Rows j in parallel; each row of each record's gradient is materialised, scaled by the
+ * record's clip factor and added, so every entry sums its records in the order i = 0..B-1. */
 int orc_layer_clipped_sum(int dtype, const void* A, const void* G, int64_t B, int64_t T,
                           int64_t d_in, int64_t d_out, const double* c, double* S) {
     if (!orc_dtype_ok(dtype)) return -1;
     const size_t es = orc_esize(dtype);
-    const int64_t band = 16;
-    const int64_t n_bands = (d_in + band - 1) / band;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t b = 0; b < n_bands; ++b) {
-        const int64_t j0 = b * band;
-        const int64_t j1 = j0 + band < d_in ? j0 + band : d_in;
-        const int64_t nj = j1 - j0;
-        double* P = (double*)malloc(sizeof(double) * (size_t)(nj * d_out));
-        double* g = (double*)malloc(sizeof(double) * (size_t)d_out);
-        for (int64_t i = 0; i < B; ++i) {
-            const char* Ai = (const char*)A + (size_t)(i * T * d_in) * es;
-            const char* Gi = (const char*)G + (size_t)(i * T * d_out) * es;
-            memset(P, 0, sizeof(double) * (size_t)(nj * d_out));
-            for (int64_t t = 0; t < T; ++t) {
-                for (int64_t k = 0; k < d_out; ++k) g[k] = orc_elem(Gi, dtype, t * d_out + k);
-                for (int64_t j = j0; j < j1; ++j) {
-                    double a = orc_elem(Ai, dtype, t * d_in + j);
-                    double* row = P + (j - j0) * d_out;
-                    for (int64_t k = 0; k < d_out; ++k) row[k] += a * g[k];
-                }
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * (size_t)d_out);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t j = 0; j < d_in; ++j) {
+            for (int64_t i = 0; i < B; ++i) {
+                const char* Ai = (const char*)A + (size_t)(i * T * d_in) * es;
+                const char* Gi = (const char*)G + (size_t)(i * T * d_out) * es;
+                orc_grad_row(dtype, Ai, Gi, T, d_in, d_out, j, row);
+                for (int64_t k = 0; k < d_out; ++k) S[j * d_out + k] += c[i] * row[k];
             }
-            for (int64_t j = j0; j < j1; ++j)
-                for (int64_t k = 0; k < d_out; ++k)
-                    S[j * d_out + k] += c[i] * P[(j - j0) * d_out + k];
         }
-        free(g);
-        free(P);
+        free(row);
     }
     return 0;
 }

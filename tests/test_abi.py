@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads and exports every function include/dpsgd.h
+declares; plan construction validates its inputs and chooses paths as documented; every argument
+error of the compute entry points is returned before any launch (on a machine without a GPU a
+launch would surface as DPSGD_ERR_HIP instead)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import differentially_private_amd as dp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dpsgd.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dpsgd_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = dp.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.check_output(["nm", "-D", "--defined-only", dp.LIB_PATH], text=True)
+    exported = set(re.findall(r"\bT (dpsgd_\w+)", dyn))
+    assert set(names) <= exported
+    assert set(names) == set(dp.EXPORTS)
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_error_strings():
+    lib = dp.load()
+    for code in (dp.OK, dp.ERR_INVALID_ARG, dp.ERR_UNSUPPORTED, dp.ERR_NONFINITE, dp.ERR_HIP, 99):
+        assert lib.dpsgd_error_string(code)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layers=[(0, 8)]), dp.ERR_INVALID_ARG),
+    (dict(layers=[(8, -1)]), dp.ERR_INVALID_ARG),
+    (dict(layers=[]), dp.ERR_INVALID_ARG),
+    (dict(dtype=7), dp.ERR_UNSUPPORTED),
+    (dict(max_records=0), dp.ERR_INVALID_ARG),
+    (dict(max_records=70000), dp.ERR_INVALID_ARG),
+    (dict(tokens=0), dp.ERR_INVALID_ARG),
+    (dict(path_policy=9), dp.ERR_UNSUPPORTED),
+    (dict(sum_policy=-1), dp.ERR_UNSUPPORTED),
+    (dict(layers=[(2**30, 2**30)], max_records=65535, tokens=2**30), dp.ERR_INVALID_ARG),
+])
+def test_plan_validation(kw, code):
+    args = dict(layers=[(8, 8)], dtype=dp.DTYPE_F32, max_records=4, tokens=4, path_policy=0,
+                sum_policy=0)
+    args.update(kw)
+    with pytest.raises(dp.DpsgdError) as e:
+        dp.Plan(args["layers"], args["dtype"], args["max_records"], args["tokens"],
+                args["path_policy"], args["sum_policy"])
+    assert e.value.code == code
+
+
+def test_path_choice_rule():
+    """Gram iff T^2 < d_in*d_out; a tie takes the direct path."""
+    p = dp.Plan([(64, 32), (768, 8), (4096, 4096), (16, 16), (17, 16)], dp.DTYPE_F32, 2, 16)
+    assert [p.layer_info(l)[0] for l in range(5)] == [dp.PATH_GRAM, dp.PATH_GRAM, dp.PATH_GRAM,
+                                                       dp.PATH_DIRECT, dp.PATH_GRAM]
+    p = dp.Plan([(768, 8), (4096, 16)], dp.DTYPE_BF16, 2, 512)
+    assert [p.layer_info(l)[0] for l in range(2)] == [dp.PATH_DIRECT, dp.PATH_DIRECT]
+    f = dp.Plan([(64, 32)], dp.DTYPE_F32, 2, 4, dp.PATH_DIRECT)
+    assert f.layer_info(0)[0] == dp.PATH_DIRECT
+
+
+def test_sum_strategy_rule_and_workspace():
+    # LoRA layers: keeping gradient blocks (8 B/param) beats re-reading T*(d_in+d_out) inputs
+    p = dp.Plan([(4096, 16), (16, 4096)] * 128, dp.DTYPE_BF16, 256, 512)
+    assert p.layer_info(0) == (dp.PATH_DIRECT, dp.SUM_STORED)
+    assert p.n_params == 16777216
+    assert p.ws_bytes >= 256 * 16777216 * 4
+    # dense layers on the Gram path always re-read A and G
+    p = dp.Plan([(4096, 4096)] * 4, dp.DTYPE_BF16, 64, 256)
+    assert p.layer_info(0) == (dp.PATH_GRAM, dp.SUM_GEMM)
+    assert p.ws_bytes < 64 << 20
+    p = dp.Plan([(768, 8)], dp.DTYPE_F32, 16, 128, dp.PATH_AUTO, dp.SUM_GEMM)
+    assert p.layer_info(0)[1] == dp.SUM_GEMM
+
+
+class _Dummy:
+    """Fake device pointers: validation must reject before anything touches them."""
+    def __init__(self, v):
+        self.v = v
+
+    def data_ptr(self):
+        return self.v
+
+
+W = _Dummy(1 << 20)      # 256-byte aligned fake workspace
+P = _Dummy(1 << 21)
+
+
+@pytest.fixture
+def plan():
+    return dp.Plan([(8, 8), (8, 4)], dp.DTYPE_F32, 4, 4)
+
+
+def _step(plan, **kw):
+    a = dict(A=[P, P], G=[P, P], out=[P, P], ws=W, C=1.0, sigma=1.0, seed=0, step_idx=0,
+             n_records=4, flags=0, stream=0)
+    a.update(kw)
+    return dp.step(plan, a["A"], a["G"], a["out"], a["ws"], a["C"], a["sigma"], a["seed"],
+                   a["step_idx"], n_records=a["n_records"], flags=a["flags"], stream=a["stream"])
+
+
+@pytest.mark.parametrize("kw", [dict(C=0.0), dict(C=-1.0), dict(C=float("nan")), dict(C=float("inf")),
+                                dict(sigma=-0.1), dict(sigma=float("nan")), dict(n_records=5),
+                                dict(n_records=-1), dict(ws=None), dict(ws=_Dummy((1 << 20) + 16)),
+                                dict(flags=8), dict(out=[P, None]), dict(A=[P, None]),
+                                dict(G=None)])
+def test_step_rejects_before_launch(plan, kw):
+    with pytest.raises(dp.DpsgdError) as e:
+        _step(plan, **kw)
+    assert e.value.code == dp.ERR_INVALID_ARG
+
+
+def test_phase_entry_points_reject_before_launch(plan):
+    lib = dp.load()
+    with pytest.raises(dp.DpsgdError):
+        dp.norms(plan, 4, 1, 3, [P, P], [P, P], W, stream=0)        # layer range
+    with pytest.raises(dp.DpsgdError):
+        dp.norms(plan, 4, 0, 2, [P, None], [P, P], W, stream=0)
+    with pytest.raises(dp.DpsgdError):
+        dp.clip(plan, 4, -2.0, W, stream=0)
+    with pytest.raises(dp.DpsgdError):
+        dp.clipped_sum(plan, 4, 0, 2, [P, P], [P, P], None, [P, None], W, stream=0)
+    with pytest.raises(dp.DpsgdError):
+        dp.noise(plan, [P, P], 1.0, float("inf"), 0, 0, stream=0)
+    with pytest.raises(dp.DpsgdError):
+        dp.layer_norm2(plan, 9, 0, 2, W, P, stream=0)
+    assert lib.dpsgd_plan_layer_info(None, 0, None, None) == dp.ERR_INVALID_ARG
+    assert lib.dpsgd_status(None, None, None) == dp.ERR_INVALID_ARG
+    assert lib.dpsgd_philox_raw(0, 0, 0, 4, None, None) == dp.ERR_INVALID_ARG
+    assert lib.dpsgd_philox_raw(0, 0, 2**64 - 2, 4, ctypes.c_void_p(P.v), None) == dp.ERR_INVALID_ARG
+    assert lib.dpsgd_plan_num_params(None) == -1
+    assert b"layer" in lib.dpsgd_last_error() or lib.dpsgd_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dp, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(dp, "_lib", None)
+    with pytest.raises(RuntimeError):
+        dp.load()
