@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the DP-SGD private-gradient step (ghost per-record norms -> clip -> clipped sum ->
+Gaussian noise) on one MI355X, through the library's C ABI.
+
+Default workload: the OPT-125M-shaped rank-8 LoRA on q,v of 12 blocks (48 linear layers,
+294,912 trainables), 16 records x 128 tokens, fp32 activations and output gradients ~ N(0,1),
+C = 1, sigma = 1.  Inputs are synthetic (the seeded generator, written straight into HBM) and
+resident before timing.  A step is one pass of the whole path over one batch.
+
+Prints one JSON line: records/s over --steps timed steps, the roofline of the dominant kernel
+(its average duration from HIP events recorded around it inside the timed loop), and the CPU
+oracle timed on the host's cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "records/sec per DP-SGD clip+noise step; % MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0}   # dense fp32 / bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, plan, dp):
+    """Per-phase algorithmic HBM bytes / flops for one physical batch of w."""
+    e = 4 if w.dtype == 0 else 2
+    B, T = w.B, w.T
+    norm_bytes = norm_flops = sum_bytes = sum_flops = 0
+    for l, (di, do) in enumerate(w.layers):
+        path, sm = plan.layer_info(l)
+        in_bytes = B * T * (di + do) * e
+        norm_bytes += in_bytes
+        if path == dp.PATH_GRAM:
+            norm_flops += 2 * B * T * T * (di + do)
+        else:
+            norm_flops += 2 * B * T * di * do
+        if sm == dp.SUM_STORED:
+            norm_bytes += B * di * do * 4            # the per-record gradient blocks written once
+            sum_bytes += B * di * do * 4 + di * do * 4
+        else:
+            sum_bytes += in_bytes + di * do * 4
+            sum_flops += 2 * B * T * di * do
+    return {"norms": (norm_bytes, norm_flops), "clipped_sum": (sum_bytes, sum_flops),
+            "noise": (8 * w.n_params, 0)}
+
+
+def device_inputs(w, datagen, torch, dev, first, n):
+    """Fill A and G of every layer for records [first, first+n) directly in HBM."""
+    import numpy as np
+    As, Gs = [], []
+    tdt = torch.float32 if w.dtype == 0 else torch.int16
+    for l, (di, do) in enumerate(w.layers):
+        for tensor, d, lst in ((0, di, As), (1, do, Gs)):
+            scale, heavy = datagen.record_params(w, l, tensor, first, n)
+            ds = torch.from_numpy(scale).to(dev)
+            dh = torch.from_numpy(heavy.astype(np.uint8)).to(dev)
+            buf = torch.empty((n, w.T, d), dtype=tdt, device=dev)
+            datagen.device_fill(w, l, tensor, buf.data_ptr(), first, n, ds.data_ptr(), dh.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+            lst.append(buf)
+    torch.cuda.synchronize()
+    return As, Gs
+
+
+def cpu_baseline(w, seconds):
+    import numpy as np  # noqa: F401
+    import datagen
+    import oracle
+    As = [datagen.host_tensor(w, l, 0) for l in range(w.n_layers)]
+    Gs = [datagen.host_tensor(w, l, 1) for l in range(w.n_layers)]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step(As, Gs, w.C, w.sigma, w.noise_seed, 0)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": w.B * reps / el, "unit": "records/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full steps of the workload ({w.B} records x {w.n_layers} layers, "
+                      f"noise included, input generation excluded), {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--manifest", default=None, help="write a run manifest JSON here")
+    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"],
+                    help="step: the benchmark; kernel: only the dominant kernel, --steps times "
+                         "(for counter collection); copy: a plain device copy of --copy-mib MiB "
+                         "(the reference for scaling HBM byte counters)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (sharding of "
+              "the step across GPUs is a design note, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    import differentially_private_amd as dp
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.mode == "copy":
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        print(json.dumps({"mode": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "ms": ms, "GBps": 8 * n / ms / 1e6}), flush=True)
+        return
+    w = datagen.workload(args.workload)
+    plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
+    ws = plan.workspace(dev)
+    As, Gs = device_inputs(w, datagen, torch, dev, 0, w.B)
+    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+    L = w.n_layers
+    stream = torch.cuda.current_stream()
+
+    if args.mode == "kernel":
+        for _ in range(args.warmup + args.steps):
+            dp.norms(plan, w.B, 0, L, As, Gs, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "kernel", "workload": w.name, "launches": args.warmup + args.steps,
+                          "algorithmic_bytes": algorithmic_work(w, plan, dp)["norms"][0]}), flush=True)
+        return
+
+    call = dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    assert dp.status(plan, ws) == dp.OK
+
+    # timed region 1: K whole steps (dpsgd_step: norms -> clip -> clipped sum -> noise)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    assert dp.status(plan, ws) == dp.OK
+
+    # timed region 2: the dominant kernel (the norm launch of the same step, same buffers),
+    # bracketed by HIP events on the stream it runs on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        dp.norms(plan, w.B, 0, L, As, Gs, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    phase_ms = {"norms": sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps}
+    phase_ms["rest_of_step"] = max(ms_per_step - phase_ms["norms"], 0.0)
+
+    work = algorithmic_work(w, plan, dp)
+    dom = "norms"
+    nbytes, nflops = work[dom]
+    dur_s = phase_ms[dom] * 1e-3
+    if nflops and nflops / max(nbytes, 1) > MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": nflops / dur_s / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / dur_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("kernel_phase") == dom and tr.get("workload") == w.name:
+            roof["traffic"] = tr.get("bytes_per_launch")
+    roof["kernel"] = {"norms": "k_norm_direct (ghost_norm, direct path)",
+                      "clipped_sum": "clipped_sum", "noise": "k_noise"}[dom]
+    roof["algorithmic_bytes"] = nbytes
+    roof["avg_ms"] = phase_ms[dom]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    value = w.B / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": value, "unit": "records/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": datagen.configs.DTYPE_NAMES[w.dtype], "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "params": w.n_params,
+                   "records_per_step": w.B, "tokens": w.T, "C": w.C, "sigma": w.sigma,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+        "phases_ms": phase_ms, "gpu_ms_per_step": gpu_ms / args.steps,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+    }
+    print(json.dumps(line), flush=True)
+    if args.manifest:
+        man = {"git": subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True,
+                                     text=True).stdout.strip() or None,
+               "torch": torch.__version__, "hip": torch.version.hip,
+               "device": torch.cuda.get_device_name(0),
+               "cu": torch.cuda.get_device_properties(0).multi_processor_count,
+               "host_cpu": platform.processor(), "nproc": os.cpu_count(),
+               "plan_paths": [plan.layer_info(l) for l in range(L)], "workload": w.name}
+        with open(args.manifest, "w") as f:
+            json.dump(man, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -204,6 +204,30 @@ def step(plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int, step_idx:
     _check(load().dpsgd_step(plan.handle, ctypes.byref(args), _stream(stream)))
 
 
+class StepCall:
+    """A dpsgd_step call with its argument block marshalled once (for training loops that call
+    the step repeatedly on the same buffers).  step_idx may be changed per call."""
+
+    def __init__(self, plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int,
+                 step_idx: int = 0, n_records: Optional[int] = None, flags: int = 0,
+                 norms_out=None, clip_out=None, stream=None):
+        self.plan = plan
+        self._keep = (_ptr_array(A), _ptr_array(G), _ptr_array(out))
+        n = plan.max_records if n_records is None else n_records
+        self.args = StepArgs(n, self._keep[0], self._keep[1], self._keep[2], _ptr(ws), C, sigma,
+                             seed, step_idx, flags, _ptr(norms_out), _ptr(clip_out))
+        self.stream = _stream(stream)
+        self._fn = load().dpsgd_step
+        self._ref = ctypes.byref(self.args)
+
+    def __call__(self, step_idx: Optional[int] = None):
+        if step_idx is not None:
+            self.args.step = step_idx
+        rc = self._fn(self.plan.handle, self._ref, self.stream)
+        if rc:
+            _check(rc)
+
+
 def status(plan: Plan, ws, stream=None) -> int:
     """Synchronise the stream and return OK or ERR_NONFINITE."""
     rc = load().dpsgd_status(plan.handle, _ptr(ws), _stream(stream))

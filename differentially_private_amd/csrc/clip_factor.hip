@@ -19,19 +19,23 @@ __global__ __launch_bounds__(1024) void k_clip(ClipArgs a) {
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int nw = blockDim.x >> 6;
-    for (int64_t rec = w; rec < a.n_rec; rec += nw) {
-        const float* p = a.parts + rec * a.parts_stride;
-        double s = 0.0;
-        for (int64_t k = lane; k < a.n_parts; k += 64) s += (double)p[k];
-        s = wave_sum_d(s);
+    for (int64_t rec0 = w; rec0 < a.n_rec; rec0 += 4 * nw) {
+        double s4[4];
+        record_norm2_x4(a.parts, a.parts_stride, a.n_parts, rec0, nw, a.n_rec, lane, s4);
         if (lane == 0) {
-            const double n = sqrt(s);
-            const double cf = (n <= a.C) ? 1.0 : a.C / n;
-            if (!isfinite(s)) atomicOr(&bad, 1u);
-            a.n_ws[rec] = (float)n;
-            a.c_ws[rec] = (float)cf;
-            if (a.n_user) a.n_user[rec] = (float)n;
-            if (a.c_user) a.c_user[rec] = (float)cf;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t rec = rec0 + j * nw;
+                if (rec >= a.n_rec) break;
+                const double s = s4[j];
+                const double n = sqrt(s);
+                const double cf = (n <= a.C) ? 1.0 : a.C / n;
+                if (!isfinite(s)) atomicOr(&bad, 1u);
+                a.n_ws[rec] = (float)n;
+                a.c_ws[rec] = (float)cf;
+                if (a.n_user) a.n_user[rec] = (float)n;
+                if (a.c_user) a.c_user[rec] = (float)cf;
+            }
         }
     }
     __syncthreads();

@@ -17,14 +17,14 @@
 namespace dpsgd {
 
 template <int DT, int MB>
-__global__ __launch_bounds__(256) void k_sum_direct(DirectArgs args) {
+__global__ __launch_bounds__(128) void k_sum_direct(DirectArgs args) {
     if (args.status && *args.status) return;
     const DirectLayer& L = args.L[blockIdx.z];
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const int tile_y = blockIdx.x / L.wg_x;
-    const int tile_x = (blockIdx.x - tile_y * L.wg_x) * 4 + w;
+    const int tile_x = (blockIdx.x - tile_y * L.wg_x) * args.wpb + w;
     if (tile_y >= L.tiles_y || tile_x >= L.tiles_x) return;
     const int n0 = tile_x * 128;
     const int m0 = tile_y * 16 * MB;
@@ -71,7 +71,17 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     const bool vec = (e + 4 <= L.n) && ((L.n & 3) == 0);
     if (vec) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t k = 0; k < a.n_src; ++k) {
+        int64_t k = 0;
+        for (; k + 8 <= a.n_src; k += 8) {     // 8 independent loads in flight, ascending order
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(L.src + (k + u) * L.n + e);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (WEIGHTED) s += a.clip[k + u] * v[u]; else s += v[u];
+            }
+        }
+        for (; k < a.n_src; ++k) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(L.src + k * L.n + e);
             if (WEIGHTED) s += a.clip[k] * v; else s += v;
         }
@@ -97,11 +107,11 @@ hipError_t launch_sum_direct(const DirectArgs& a, int dtype, int mb, int n_split
     }
     const dim3 grid(gx, n_splits, a.n_layers);
     if (dtype == kBF16) {
-        if (mb == 1) hipLaunchKernelGGL((k_sum_direct<kBF16, 1>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_sum_direct<kBF16, 2>), grid, dim3(256), 0, s, a);
+        if (mb == 1) hipLaunchKernelGGL((k_sum_direct<kBF16, 1>), grid, dim3(64 * a.wpb), 0, s, a);
+        else hipLaunchKernelGGL((k_sum_direct<kBF16, 2>), grid, dim3(64 * a.wpb), 0, s, a);
     } else {
-        if (mb == 1) hipLaunchKernelGGL((k_sum_direct<kF32, 1>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_sum_direct<kF32, 2>), grid, dim3(256), 0, s, a);
+        if (mb == 1) hipLaunchKernelGGL((k_sum_direct<kF32, 1>), grid, dim3(64 * a.wpb), 0, s, a);
+        else hipLaunchKernelGGL((k_sum_direct<kF32, 2>), grid, dim3(64 * a.wpb), 0, s, a);
     }
     return hipGetLastError();
 }

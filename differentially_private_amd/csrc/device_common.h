@@ -11,6 +11,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// x if keep, else +0.  An integer AND instead of a select, so that the compiler
+// keeps the load that produced x unconditional (a select lets it sink the load
+// into a branch followed by an immediate wait, which serialises a batch of loads).
+__device__ __forceinline__ float keep_or_zero(float x, bool keep) {
+    return __uint_as_float(__float_as_uint(x) & (keep ? 0xFFFFFFFFu : 0u));
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
@@ -27,6 +34,45 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
+}
+
+// Squared norms of up to four records from their partials (record r's partials
+// at parts + r * stride, n_parts of them): every lane sums partials lane,
+// lane + 64, ... in ascending order in fp64 (a partial past the end adds +0,
+// which changes no sum of squares), then a fixed butterfly combines the lanes.  The per-record order depends only on n_parts, never on which or how
+// many records are reduced together, so every caller gets bitwise the same
+// value for a record.  Records >= n_rec are skipped (their result is 0).
+__device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts, int64_t stride,
+                                                int64_t n_parts, int64_t rec0, int64_t rec_step,
+                                                int64_t n_rec, int lane, double (&out)[4]) {
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    const float* p[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t rec = rec0 + j * rec_step;
+        ok[j] = rec < n_rec;
+        p[j] = parts + (ok[j] ? rec : 0) * stride;
+    }
+    // batches of 8 partials per lane and record: 32 independent loads in flight.  Every
+    // load reads an in-bounds address (clamped) and the value is masked afterwards, so the
+    // loads are unconditional and issue back to back.
+    for (int64_t k0 = lane; k0 < n_parts; k0 += 64 * 8) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t k = k0 + 64 * u;
+            const int64_t kc = k < n_parts ? k : n_parts - 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j][u] = keep_or_zero(p[j][kc], ok[j] && k < n_parts);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] += (double)v[j][u];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = wave_sum_d(s[j]);
 }
 
 // v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of the A block and

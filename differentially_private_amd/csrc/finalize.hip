@@ -1,0 +1,142 @@
+// Fused tail of the step for plans whose layers all keep their per-record
+// gradient blocks (the STORED clipped-sum strategy): in one launch over the
+// flat parameter index e,
+//   out[e] (+)= sum_i c_i P_i[e] + sigma * C * Z[e]
+// ("Privacy-Preserving Machine Learning", DP-SGD phases 3-4: clip each record,
+// sum, add N(0, sigma^2 C^2 I) once).  When the partials are few, every block
+// first recomputes all clip factors itself with exactly the arithmetic of the
+// clip_factor kernel (one wavefront per record, lanes striding the record's
+// partials in a fixed order, fp64 butterfly), so the factors are bitwise the
+// ones clip_factor would produce and no separate launch is needed; block 0
+// publishes n_i, c_i and the status word.  Otherwise the factors come from a
+// preceding clip_factor launch.  A nonfinite norm skips every write to out.
+#include <algorithm>
+
+#include "philox.h"
+
+namespace dpsgd {
+
+constexpr int kFinalBatch = 16;  // records whose blocks a thread loads before the clip prologue
+
+// Grid: x = 256-thread chunks of a layer (4 elements per thread), y = layer of the
+// launch.  Element x of layer l has flat index off_l + x.
+template <bool CLIP_INSIDE>
+__global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
+    __shared__ float cs[kFinalMaxRecords];
+    __shared__ uint32_t bad;
+    const int tid = threadIdx.x;
+    const int l = blockIdx.y;
+    const int64_t off = a.off[l];
+    const int64_t n_l = a.off[l + 1] - off;
+    const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + tid) * 4;
+    const bool active = x0 < n_l;
+    const bool vec = active && x0 + 4 <= n_l && (n_l & 3) == 0 && (off & 3) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.src[l])) & 15u) == 0;
+    const float* src = a.src[l] + x0;
+
+    // 1) the first batch of this thread's gradient-block loads, independent of the factors
+    f32x4 v[kFinalBatch];
+    const int64_t nb0 = a.n_rec < kFinalBatch ? a.n_rec : kFinalBatch;
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < kFinalBatch; ++u)   // unconditional: rows past n_rec repeat the last
+            v[u] = *reinterpret_cast<const f32x4*>(src + (u < nb0 ? u : nb0 - 1) * n_l);
+    }
+
+    // 2) this thread's normals (Philox + Box-Muller), computed while the loads are in flight
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.noise && vec) gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
+
+    // 3) clip factors
+    const float* cf = a.clip;
+    bool skip;
+    if (CLIP_INSIDE) {
+        const uint32_t old = a.accumulate ? *a.status : 0u;
+        if (tid == 0) bad = 0u;
+        __syncthreads();
+        const int w = tid >> 6, lane = tid & 63;
+        for (int64_t rec0 = w; rec0 < a.n_rec; rec0 += 16) {
+            double s4[4];
+            record_norm2_x4(a.parts, a.parts_stride, a.n_parts, rec0, 4, a.n_rec, lane, s4);
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t rec = rec0 + 4 * j;
+                    if (rec >= a.n_rec) break;
+                    const double s = s4[j];
+                    const double n = sqrt(s);
+                    const double c = (n <= a.C) ? 1.0 : a.C / n;
+                    if (!isfinite(s)) atomicOr(&bad, 1u);
+                    cs[rec] = (float)c;
+                    if (blockIdx.x == 0 && l == 0) {
+                        a.n_ws[rec] = (float)n;
+                        a.c_ws[rec] = (float)c;
+                        if (a.n_user) a.n_user[rec] = (float)n;
+                        if (a.c_user) a.c_user[rec] = (float)c;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (blockIdx.x == 0 && l == 0 && tid == 0) *a.status = old | bad;
+        skip = (old | bad) != 0u;
+        cf = cs;
+    } else {
+        skip = *a.status != 0u;
+    }
+    if (skip || !active) return;
+
+    // 4) out (+)= sum_i c_i P_i (ascending i) + sigma C Z
+    if (vec) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kFinalBatch; ++u) s += keep_or_zero(cf[u < nb0 ? u : 0], u < nb0) * v[u];
+        for (int64_t i = kFinalBatch; i < a.n_rec; i += 8) {   // further records, 8 loads at a time
+            f32x4 w8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t r = i + u < a.n_rec ? i + u : a.n_rec - 1;
+                w8[u] = *reinterpret_cast<const f32x4*>(src + r * n_l);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                s += keep_or_zero(cf[i + u < a.n_rec ? i + u : 0], i + u < a.n_rec) * w8[u];
+        }
+        f32x4* o = reinterpret_cast<f32x4*>(a.out[l] + x0);
+        if (a.accumulate) s = *o + s;
+        s[0] += a.scale * z[0];
+        s[1] += a.scale * z[1];
+        s[2] += a.scale * z[2];
+        s[3] += a.scale * z[3];
+        *o = s;
+        return;
+    }
+    for (int q = 0; q < 4; ++q) {
+        const int64_t x = x0 + q;
+        if (x >= n_l) break;
+        const uint64_t e = (uint64_t)(off + x);
+        float z = 0.f;
+        if (a.noise) {
+            float z4[4];
+            gauss4(e >> 2, a.step, a.seed, z4);
+            z = z4[e & 3];
+        }
+        float s = 0.f;
+        for (int64_t i = 0; i < a.n_rec; ++i) s += cf[i] * a.src[l][i * n_l + x];
+        float* o = a.out[l] + x;
+        if (a.accumulate) s = *o + s;
+        *o = s + a.scale * z;
+    }
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s) {
+    int64_t max_n = 0;
+    for (int l = 0; l < a.n_layers; ++l) max_n = std::max<int64_t>(max_n, a.off[l + 1] - a.off[l]);
+    if (max_n == 0) return hipSuccess;
+    const dim3 grid((unsigned)((max_n + 1023) / 1024), a.n_layers);
+    if (clip_inside) hipLaunchKernelGGL(k_finalize<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_finalize<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dpsgd

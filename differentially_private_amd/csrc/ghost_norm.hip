@@ -17,14 +17,17 @@
 
 namespace dpsgd {
 
+// fp32, MB = 1 (LoRA shapes): ask for at least 4 wavefronts per SIMD (the kernel
+// then fits 5 without spilling), so that a whole LoRA workload's tiles are
+// resident at once and no tail of late wavefronts is left.
 template <int DT, int MB, bool STORE>
-__global__ __launch_bounds__(256) void k_norm_direct(DirectArgs args) {
+__global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_direct(DirectArgs args) {
     const DirectLayer& L = args.L[blockIdx.z];
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const int tile_y = blockIdx.x / L.wg_x;
-    const int tile_x = (blockIdx.x - tile_y * L.wg_x) * 4 + w;
+    const int tile_x = (blockIdx.x - tile_y * L.wg_x) * args.wpb + w;
     if (tile_y >= L.tiles_y || tile_x >= L.tiles_x) return;
     const int n0 = tile_x * 128;
     const int m0 = tile_y * 16 * MB;
@@ -176,7 +179,7 @@ hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store
         if (v > gx) gx = v;
     }
     const dim3 grid(gx, (unsigned)a.n_rec, a.n_layers);
-#define DPSGD_LAUNCH(DT, MB, ST) hipLaunchKernelGGL((k_norm_direct<DT, MB, ST>), grid, dim3(256), 0, s, a)
+#define DPSGD_LAUNCH(DT, MB, ST) hipLaunchKernelGGL((k_norm_direct<DT, MB, ST>), grid, dim3(64 * a.wpb), 0, s, a)
     if (dtype == kBF16) {
         if (mb == 1) { if (store) DPSGD_LAUNCH(kBF16, 1, true); else DPSGD_LAUNCH(kBF16, 1, false); }
         else { if (store) DPSGD_LAUNCH(kBF16, 2, true); else DPSGD_LAUNCH(kBF16, 2, false); }

@@ -24,7 +24,7 @@ struct DirectLayer {
     int32_t x_is_in;    // 1: X = A (d_in), Y = G (d_out); 0: X = G, Y = A
     int32_t tiles_x;    // ceil(dX / 128)
     int32_t tiles_y;    // ceil(dY / (16*MB))
-    int32_t wg_x;       // ceil(tiles_x / 4)
+    int32_t wg_x;       // ceil(tiles_x / waves per workgroup)
     int32_t part_off;   // first norm partial of this layer
     int32_t vec_x;      // X rows are 16-byte aligned (vector loads allowed)
     int64_t d_out;      // for output addressing
@@ -35,6 +35,8 @@ struct DirectArgs {
     DirectLayer L[kMaxLaunchLayers];
     int32_t n_layers;
     int32_t accumulate;        // SUM with direct write: out += tile
+    int32_t wpb;               // wavefronts per workgroup (1..8), one column tile each
+    int32_t pad;
     int64_t T;
     int64_t n_rec;
     int64_t parts_stride;      // partials per record (record-major partial array)
@@ -105,6 +107,38 @@ struct NoiseArgs {
     const uint32_t* status;
 };
 
+constexpr int kFinalMaxLayers = 48;
+constexpr int kFinalMaxRecords = 1024;      // records whose factors a block recomputes itself
+constexpr int64_t kFinalMaxClipWork = 65536;  // records x partials a block reduces itself
+
+// Fused tail of a step whose layers all keep their per-record gradient blocks:
+// clip factors (recomputed per block from the partials, or read), the weighted
+// sum over records and the noise, in one pass over the flat parameter index.
+struct FinalizeArgs {
+    float* out[kFinalMaxLayers];
+    const float* src[kFinalMaxLayers];     // stored gradient blocks [max_records][n_l]
+    int64_t off[kFinalMaxLayers + 1];      // flat offsets of the launch's layers
+    int32_t n_layers;
+    int32_t accumulate;
+    int32_t noise;
+    int32_t pad;
+    int64_t n_rec;
+    uint64_t seed, step;
+    float scale;                           // sigma * C
+    // clip factors computed inside (first variant) ...
+    const float* parts;
+    int64_t parts_stride;
+    int64_t n_parts;
+    double C;
+    float* n_ws;
+    float* c_ws;
+    float* n_user;
+    float* c_user;
+    uint32_t* status;
+    // ... or read (second variant)
+    const float* clip;
+};
+
 struct LayerNormArgs {
     const float* parts;
     int64_t parts_stride;
@@ -127,5 +161,6 @@ hipError_t launch_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block,
                              uint32_t* out, hipStream_t s);
 hipError_t launch_layer_norm2(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s);
 
 }  // namespace dpsgd

@@ -80,12 +80,58 @@ __device__ __forceinline__ void direct_block_bf16(const uint16_t* __restrict__ X
     }
 }
 
-// ---- fp32: 16 tokens per step in 4 MFMA k-steps of 4, lane (g, c) holds token 4s + g ----
+// ---- fp32: MFMA 16x16x4 takes one token per lane: lane (g, c) holds token 4s + g ----
+// The token rows are processed in half-steps of 8: the loads of one half are in
+// flight while the MFMAs of the other run.
+template <int MB>
+__device__ __forceinline__ void load_half_f32(const float* __restrict__ X, const float* __restrict__ Y,
+                                              int64_t T, int dX, int dY, int m0, int g, int c,
+                                              int64_t t0, const int (&cols)[2], const bool (&full)[2],
+                                              f32x4 (&xv)[2][2], float (&yv)[2][MB]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t t = t0 + 4 * s + g;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (t < T && full[h]) {
+                xv[s][h] = *reinterpret_cast<const f32x4*>(X + t * dX + cols[h]);
+            } else {
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (t < T) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        v[u] = (cols[h] + u < dX) ? X[t * dX + cols[h] + u] : 0.f;
+                }
+                xv[s][h] = v;
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = m0 + 16 * mb + c;
+            yv[s][mb] = (t < T && m < dY) ? Y[t * dY + m] : 0.f;
+        }
+    }
+}
+
+template <int MB>
+__device__ __forceinline__ void mfma_half_f32(const f32x4 (&xv)[2][2], const float (&yv)[2][MB],
+                                              f32x4 (&acc)[MB][8]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[mb][h * 4 + j] = mfma_f32(yv[s][mb], xv[s][h][j], acc[mb][h * 4 + j]);
+}
+
 template <int MB>
 __device__ __forceinline__ void direct_block_f32(const float* __restrict__ X,
-                                                 const float* __restrict__ Y, int64_t T, int dX,
-                                                 int dY, int n0, int m0, bool vec_x, int g, int c,
-                                                 f32x4 (&acc)[MB][8]) {
+                                                      const float* __restrict__ Y, int64_t T,
+                                                      int dX, int dY, int n0, int m0, bool vec_x,
+                                                      int g, int c, f32x4 (&acc)[MB][8]) {
     int cols[2];
     bool full[2];
 #pragma unroll
@@ -93,41 +139,15 @@ __device__ __forceinline__ void direct_block_f32(const float* __restrict__ X,
         cols[h] = n0 + 64 * h + 4 * c;
         full[h] = vec_x && (cols[h] + 4 <= dX);
     }
+    f32x4 xa[2][2], xb[2][2];
+    float ya[2][MB], yb[2][MB];
+    load_half_f32<MB>(X, Y, T, dX, dY, m0, g, c, 0, cols, full, xa, ya);
     for (int64_t t0 = 0; t0 < T; t0 += 16) {
-        f32x4 xv[4][2];
-        float yv[4][MB];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int64_t t = t0 + 4 * s + g;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (t < T && full[h]) {
-                    xv[s][h] = *reinterpret_cast<const f32x4*>(X + t * dX + cols[h]);
-                } else {
-                    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                    if (t < T) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            v[u] = (cols[h] + u < dX) ? X[t * dX + cols[h] + u] : 0.f;
-                    }
-                    xv[s][h] = v;
-                }
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int m = m0 + 16 * mb + c;
-                yv[s][mb] = (t < T && m < dY) ? Y[t * dY + m] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[mb][h * 4 + j] = mfma_f32(yv[s][mb], xv[s][h][j], acc[mb][h * 4 + j]);
+        if (t0 + 8 < T) load_half_f32<MB>(X, Y, T, dX, dY, m0, g, c, t0 + 8, cols, full, xb, yb);
+        mfma_half_f32<MB>(xa, ya, acc);
+        if (t0 + 8 >= T) break;
+        if (t0 + 16 < T) load_half_f32<MB>(X, Y, T, dX, dY, m0, g, c, t0 + 16, cols, full, xa, ya);
+        mfma_half_f32<MB>(xb, yb, acc);
     }
 }
 

@@ -55,6 +55,7 @@ def _load():
             "orc_philox_words": (None, [_U64, _U64, _U64, _U64, _P]),
             "orc_gauss": (None, [_U64, _U64, _U64, _I64, _P]),
             "orc_add_noise": (None, [_P, _I64, _U64, _D, _D, _U64, _U64]),
+            "orc_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -62,6 +63,11 @@ def _load():
             f.argtypes = args
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return _load().orc_num_threads()
 
 
 def _dtype_of(x: np.ndarray) -> int:

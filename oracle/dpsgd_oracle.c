@@ -29,6 +29,7 @@
  * patterns, widened exactly to double.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -226,3 +227,6 @@ void orc_add_noise(double* S, int64_t n, uint64_t first_e, double sigma, double 
     for (int64_t q = 0; q < n; ++q) S[q] += s * z[q];
     free(z);
 }
+
+/* Threads the oracle's parallel loops use (for reporting). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
