@@ -74,6 +74,16 @@ def device_inputs(w, datagen, torch, dev, first, n):
     return As, Gs
 
 
+def kernel_src_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "differentially_private_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def cpu_baseline(w, seconds):
     import numpy as np  # noqa: F401
     import datagen
@@ -202,9 +212,13 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic))
-        if tr.get("kernel_phase") == dom and tr.get("workload") == w.name:
+    tpath = args.traffic or os.path.join(ROOT, "profiles", "norm_kernel_traffic.json")
+    if os.path.exists(tpath):
+        # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a plain copy of
+        # known size), valid only while the kernel sources are the ones it was measured on
+        tr = json.load(open(tpath))
+        if (tr.get("kernel_phase") == dom and tr.get("workload") == w.name
+                and tr.get("src_hash") == kernel_src_hash()):
             roof["traffic"] = tr.get("bytes_per_launch")
     roof["kernel"] = {"norms": "k_norm_direct (ghost_norm, direct path)",
                       "clipped_sum": "clipped_sum", "noise": "k_noise"}[dom]

@@ -106,8 +106,9 @@ def gather(w: Workload, layer: int, tensor: int, rec, tok, col) -> np.ndarray:
     tok = np.ascontiguousarray(tok, dtype=np.int64)
     col = np.ascontiguousarray(col, dtype=np.int64)
     n = rec.size
-    scale = np.array([w.record_scale(layer, tensor, int(r)) for r in rec], dtype=np.float64)
-    heavy = np.array([w.record_heavy(int(r)) for r in rec], dtype=np.uint8)
+    uniq, inv = np.unique(rec, return_inverse=True)
+    scale = np.array([w.record_scale(layer, tensor, int(r)) for r in uniq], dtype=np.float64)[inv]
+    heavy = np.array([w.record_heavy(int(r)) for r in uniq], dtype=np.uint8)[inv]
     out = np.empty(n, dtype=np.float32)
     d = tensor_dim(w, layer, tensor)
     rc = _load_host().dg_gather_host(w.data_seed, layer, tensor, w.dtype, w.T, d, n,

@@ -67,3 +67,42 @@ def gpu_step(w, As, Gs, dev, C=None, sigma=None, seed=0, step=0, flags=0, path=0
 
 def flat(xs):
     return np.concatenate([np.asarray(x, dtype=np.float64).reshape(-1) for x in xs])
+
+
+def device_tensor(w, layer, tensor, first, n, dev):
+    """Generator output for records [first, first+n) of (layer, tensor), filled directly in HBM."""
+    import torch
+    scale, heavy = datagen.record_params(w, layer, tensor, first, n)
+    ds = torch.from_numpy(scale).to(dev)
+    dh = torch.from_numpy(heavy).to(dev)
+    d = datagen.tensor_dim(w, layer, tensor)
+    buf = torch.empty((n, w.T, d), dtype=torch.float32 if w.dtype == F32 else torch.int16,
+                      device=dev)
+    datagen.device_fill(w, layer, tensor, buf.data_ptr(), first, n, ds.data_ptr(), dh.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    return buf
+
+
+def oracle_record_layer_norm2(w, rec, layers):
+    """Oracle squared norm of record `rec`'s gradient in each of `layers` (inputs regenerated)."""
+    import oracle
+    out = []
+    for l in layers:
+        A = datagen.host_tensor(w, l, 0, rec, 1)
+        G = datagen.host_tensor(w, l, 1, rec, 1)
+        out.append(oracle.layer_norm2(A, G)[0])
+    return np.array(out)
+
+
+def oracle_sum_entry(w, layer, j, k, c, first=0, n=None):
+    """Oracle S_layer[j, k] = sum_i c_i sum_t A[i,t,j] G[i,t,k] over records [first, first+n),
+    from gathered columns of the generator (the gradient entry of every record, weighted)."""
+    import oracle
+    n = w.B if n is None else n
+    rec = np.repeat(np.arange(first, first + n), w.T)
+    tok = np.tile(np.arange(w.T), n)
+    a = datagen.gather(w, layer, 0, rec, tok, np.full(rec.size, j))
+    g = datagen.gather(w, layer, 1, rec, tok, np.full(rec.size, k))
+    S = oracle.layer_clipped_sum(a.reshape(n, w.T, 1), g.reshape(n, w.T, 1),
+                                 np.asarray(c, dtype=np.float64))
+    return S[0, 0]
