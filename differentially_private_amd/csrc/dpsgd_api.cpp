@@ -70,6 +70,7 @@ struct LayerPlan {
     int64_t n_parts, part_off;
     int64_t stored_off;  // bytes into ws (STORED)
     int64_t split_off;   // bytes into ws (GEMM with splits)
+    bool dense;          // GEMM sum on the 256x128-tile dense kernel (bf16, both dimensions > 16)
 };
 
 struct dpsgd_plan {
@@ -78,7 +79,8 @@ struct dpsgd_plan {
     int64_t B, T;
     int64_t parts_total;
     int64_t n_params;
-    int n_splits_max;
+    int n_splits_max;        // tile-engine GEMM sums
+    int n_splits_dense_max;  // dense GEMM sums
     int64_t status_off, parts_off, n_off, c_off;
     int64_t ws_bytes;
 };
@@ -292,7 +294,73 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
     }
     if (n_rec == 0) return DPSGD_OK;
 
-    // 2) GEMM layers: tile-engine sum, split over records, then a fixed-order reduce
+    // 2) dense GEMM layers (bf16): 256x128-tile MFMA kernel, split over records
+    {
+        int nsd = (int)std::min<int64_t>(p->n_splits_dense_max, n_rec);
+        const int64_t rpsd = (n_rec + nsd - 1) / nsd;
+        nsd = (int)((n_rec + rpsd - 1) / rpsd);
+        DenseSumArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.accumulate = acc;
+        a.T = p->T;
+        a.n_rec = n_rec;
+        a.rec_per_split = rpsd;
+        a.clip = clip;
+        a.status = status;
+        ReduceArgs r;
+        std::memset(&r, 0, sizeof(r));
+        r.accumulate = acc;
+        r.n_src = nsd;
+        r.status = status;
+        auto flush = [&]() -> int {
+            if (!a.n_layers) return DPSGD_OK;
+            hipError_t e = launch_sum_dense(a, nsd, s);
+            if (e != hipSuccess) return hip_fail(e, "clipped_sum (dense) launch");
+            if (nsd > 1) {
+                e = launch_reduce(r, false, s);
+                if (e != hipSuccess) return hip_fail(e, "clipped_sum (split reduce) launch");
+            }
+            a.n_layers = 0;
+            r.n_layers = 0;
+            r.max_n4 = 0;
+            return DPSGD_OK;
+        };
+        for (int l = l0; l < l1; ++l) {
+            const LayerPlan& lp = p->layers[l];
+            if (lp.sum_mode != DPSGD_SUM_GEMM || !lp.dense) continue;
+            DenseSumLayer& d = a.L[a.n_layers];
+            d.A = A[l - l0];
+            d.G = G[l - l0];
+            d.d_in = (int32_t)lp.d_in;
+            d.d_out = (int32_t)lp.d_out;
+            d.tiles_m = (int32_t)((lp.d_in + 255) / 256);
+            d.tiles_n = (int32_t)((lp.d_out + 127) / 128);
+            d.vec_a = ptr_aligned16(d.A) && ((lp.d_in * es) % 16 == 0);
+            d.vec_g = ptr_aligned16(d.G) && ((lp.d_out * es) % 16 == 0);
+            if (nsd > 1) {
+                d.split = ws_f(ws, lp.split_off);
+                d.split_stride = lp.n_params;
+                d.out = nullptr;
+                ReduceLayer& rl = r.L[r.n_layers++];
+                rl.src = d.split;
+                rl.out = out[l - l0];
+                rl.n = lp.n_params;
+                r.max_n4 = std::max<int64_t>(r.max_n4, (lp.n_params + 3) / 4);
+            } else {
+                d.out = out[l - l0];
+                d.split = nullptr;
+                d.split_stride = 0;
+            }
+            if (++a.n_layers == kDenseMaxLayers) {
+                int rc = flush();
+                if (rc) return rc;
+            }
+        }
+        int rc = flush();
+        if (rc) return rc;
+    }
+
+    // 3) other GEMM layers: tile-engine sum, split over records, then a fixed-order reduce
     for (int mb = 1; mb <= 2; ++mb) {
         DirectArgs a;
         std::memset(&a, 0, sizeof(a));
@@ -323,7 +391,7 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
         };
         for (int l = l0; l < l1; ++l) {
             const LayerPlan& lp = p->layers[l];
-            if (lp.sum_mode != DPSGD_SUM_GEMM || lp.tiles.mb != mb) continue;
+            if (lp.sum_mode != DPSGD_SUM_GEMM || lp.dense || lp.tiles.mb != mb) continue;
             DirectLayer& d = a.L[a.n_layers];
             const void* a_ptr = A[l - l0];
             const void* g_ptr = G[l - l0];
@@ -511,13 +579,26 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
         return fail(DPSGD_ERR_INVALID_ARG, "too many norm partials");
     }
 
-    // split count of the GEMM clipped sum: aim for ~8192 wavefronts per launch
-    int64_t waves = 0;
-    for (const LayerPlan& lp : p->layers)
-        if (lp.sum_mode == DPSGD_SUM_GEMM) waves += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
-    int ns = 1;
-    if (waves > 0) ns = (int)std::min<int64_t>(std::min<int64_t>(p->B, 64), std::max<int64_t>(1, (8192 + waves - 1) / waves));
+    // split counts of the GEMM clipped sums: ~8192 wavefronts per launch for the tile
+    // engine, >= 512 workgroups (two per CU) for the dense kernel (256 x 128 tiles)
+    int64_t waves = 0, dense_wgs = 0;
+    for (LayerPlan& lp : p->layers) {
+        if (lp.sum_mode != DPSGD_SUM_GEMM) continue;
+        lp.dense = p->dtype == DPSGD_DTYPE_BF16 && lp.tiles.mb == 2;
+        if (lp.dense)
+            dense_wgs += ((lp.d_in + 255) / 256) * ((lp.d_out + 127) / 128);
+        else
+            waves += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
+    }
+    auto splits_for = [&](int64_t units, int64_t target) -> int {
+        if (units <= 0) return 1;
+        return (int)std::min<int64_t>(std::min<int64_t>(p->B, 64),
+                                      std::max<int64_t>(1, (target + units - 1) / units));
+    };
+    const int ns = splits_for(waves, 8192);
+    const int nsd = splits_for(dense_wgs, 512);
     p->n_splits_max = ns;
+    p->n_splits_dense_max = nsd;
 
     // workspace layout
     int64_t off = 0;
@@ -533,9 +614,9 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
         if (lp.sum_mode == DPSGD_SUM_STORED) {
             lp.stored_off = off;
             off = align_up(off + p->B * lp.n_params * 4);
-        } else if (ns > 1) {
+        } else if ((lp.dense ? nsd : ns) > 1) {
             lp.split_off = off;
-            off = align_up(off + (int64_t)ns * lp.n_params * 4);
+            off = align_up(off + (int64_t)(lp.dense ? nsd : ns) * lp.n_params * 4);
         }
     }
     p->ws_bytes = off;

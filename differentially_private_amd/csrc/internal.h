@@ -139,6 +139,31 @@ struct FinalizeArgs {
     const float* clip;
 };
 
+constexpr int kDenseMaxLayers = 32;
+
+// Dense clipped sum (bf16, both dimensions wide): 256 x 128 output tiles.
+struct DenseSumLayer {
+    const void* A;       // [n_rec, T, d_in]
+    const void* G;       // [n_rec, T, d_out]
+    float* out;          // [d_in, d_out] (used when split_stride == 0)
+    float* split;        // [n_splits][d_in * d_out] split partials
+    int32_t d_in, d_out;
+    int32_t tiles_m, tiles_n;
+    int32_t vec_a, vec_g;
+    int64_t split_stride;
+};
+
+struct DenseSumArgs {
+    DenseSumLayer L[kDenseMaxLayers];
+    int32_t n_layers;
+    int32_t accumulate;
+    int64_t T;
+    int64_t n_rec;
+    int64_t rec_per_split;
+    const float* clip;
+    const uint32_t* status;
+};
+
 struct LayerNormArgs {
     const float* parts;
     int64_t parts_stride;
@@ -162,5 +187,6 @@ hipError_t launch_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block,
 hipError_t launch_layer_norm2(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s);
+hipError_t launch_sum_dense(const DenseSumArgs& a, int n_splits, hipStream_t s);
 
 }  // namespace dpsgd
