@@ -4,19 +4,27 @@
 // Inflation ...", Eq. 3), an MFMA GEMM with M = d_in, N = d_out and the
 // reduction over the n_records * T token rows.
 //
-// Workgroup tile 256 (d_in) x 128 (d_out), 4 wavefronts of 128 x 64 (32 MFMAs
-// per k-step each), two workgroups per CU, k-step 32 tokens (one
-// v_mfma_f32_16x16x32_bf16 deep).  Both
-// operands are stored with the reduction axis (tokens) as rows, so each k-step is
-// staged through LDS transposed: a thread loads an 8 token x 8 column block
-// (16-byte loads), transposes it in registers and writes 8 column vectors of 8
-// tokens, so the MFMA operands are single 16-byte LDS reads.  Pitch 48 elements
-// (96 bytes): measured on gfx950, the 16-lane operand reads then take 4 cycles
-// (conflict-free; 8 at 80/112/144 bytes) and the staging writes 16.  Global loads
-// run two k-steps ahead of the MFMAs (a register ring of two slots, the loop
-// unrolled by two so that each slot stays in fixed registers: 244 VGPRs, no
-// scratch), LDS is double-buffered with one barrier per k-step, and the second
-// workgroup on the CU computes while the first waits.
+// Workgroup tile 256 (d_in) x 128 (d_out), 4 wavefronts of 128 x 64 (32
+// v_mfma_f32_16x16x32_bf16 per k-step each), two workgroups per CU, k-step 32
+// tokens.  Both operands are stored with the reduction axis (tokens) as rows, so
+// the MFMA operands (8 consecutive tokens of one column per lane) are a transpose
+// of what memory holds.  Two kernels:
+//
+// k_sum_dense_dma (T a multiple of 32, rows 16-byte aligned): each k-step tile is
+// copied token-major into LDS by global_load_lds_dwordx4 (no registers, no VALU),
+// three LDS stages with loads two k-steps ahead and one barrier per k-step, and
+// the operands come out of LDS through ds_read_b64_tr_b16: within each 16-lane
+// group, result lane i element e is element i % 4 of what lane 4e + i / 4 read,
+// so lane 4e + p points at columns 4p..4p+3 of token row e and two such reads give
+// one MFMA operand.  The 16-byte chunk c of token row r sits at chunk c ^ swz(r),
+// which spreads each half-wave's transposed reads over all banks.
+//
+// k_sum_dense_bf16 (any T, any alignment): each k-step is loaded into registers as
+// 8 token x 8 column blocks (16-byte loads, zero-filled past T and d), transposed
+// in registers and written as column vectors (pitch 96 bytes: the 16-lane operand
+// reads are conflict-free, the staging writes take 16 cycles), two k-steps of
+// loads in flight in a two-slot register ring (loop unrolled by two so each slot
+// stays in fixed registers), LDS double-buffered.
 //
 // The per-record factor is applied to the fp32 accumulator, never to the bf16
 // operands: with acc holding sum_{j<=i} (c_j / c_i) P_j during record i, the
@@ -83,7 +91,238 @@ __device__ __forceinline__ void store_step(uint16_t* Xs, const Loader& ld, const
     }
 }
 
+constexpr int kStages = 3;                       // LDS stages of the copy kernel
+constexpr int kStageElems = (kTM + kTN) * kTK;   // 12288 bf16 (24 KB): A rows, then G rows
+constexpr int kGOff = kTM * kTK;                 // G part of a stage
+constexpr int kGroupM = 8;                       // tile rows per group of the tile order
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Physical 16-byte chunk of logical chunk c in token row r of a staged k-step is c ^ swz(r):
+// the transposed reads of one half-wave (token rows 8g + 4h + 0..3 for g in {0, 1}, two chunks
+// each) then fall on 16 distinct chunk slots of the 256-byte bank space.
+__device__ __forceinline__ int swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
+// Written out so that the compiler does not track it as an LDS store: it would otherwise wait
+// for every copy in flight (vmcnt(0)) before each LDS read and barrier, since it cannot tell
+// the stages apart.  Completion is awaited explicitly (vmcnt) before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* l) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(l));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Clip factors of records base .. base + 63, one per lane (1 past the end), so that a record
+// boundary inside the k-loop reads its factor with v_readlane instead of a vector load whose
+// wait would also drain the operand loads in flight.
+struct ClipWindow {
+    int64_t base;
+    float v;
+    __device__ __forceinline__ void load(const float* clip, int64_t b, int64_t end, int lane) {
+        base = b;
+        v = (b + lane < end) ? clip[b + lane] : 1.f;
+        asm volatile("" ::"v"(v));   // consume the load here: no wait at the join after a reload
+    }
+    __device__ __forceinline__ float get(const float* clip, int64_t rec, int64_t end, int lane) {
+        if (rec - base >= 64) load(clip, rec, end, lane);
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)(rec - base)));
+    }
+};
+
+// Tile of this workgroup.  Workgroup ids go round-robin over the 8 XCDs (ids x, x + 8, ... run
+// on XCD x); those get consecutive logical ids, and logical ids walk groups of kGroupM tile rows
+// column by column, so the ~64 workgroups resident on one XCD cover an 8 x 8 block of tiles and
+// read 8 A column bands and 8 G column bands through that XCD's L2.
+__device__ __forceinline__ bool tile_of(const DenseSumLayer& L, int& tm, int& tn) {
+    const int n_tiles = L.tiles_m * L.tiles_n;
+    int t = blockIdx.x;
+    if (t >= n_tiles) return false;
+    if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
+    const int group = t / (kGroupM * L.tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(L.tiles_m - first_m, kGroupM);
+    const int r = t - group * kGroupM * L.tiles_n;
+    tm = first_m + r % gm;
+    tn = r / gm;
+    return true;
+}
+
+// Writes scale * acc for wave tile (wm, wn); lane (g, c) holds rows 4g + r, column c of each
+// 16 x 16 block.
+__device__ __forceinline__ void store_tile(const DenseSumLayer& L, int accumulate, int64_t split,
+                                           int m0, int n0, int wm, int wn, int g, int c,
+                                           float scale, const f32x4 (&acc)[8][4]) {
+    float* dst = L.out;
+    bool add = accumulate != 0;
+    if (L.split_stride) {
+        dst = L.split + split * L.split_stride;
+        add = false;
+    }
+    const int64_t d_out = L.d_out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + wm * 128 + 16 * i + 4 * g + r;
+            if (row >= L.d_in) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + wn * 64 + 16 * j + c;
+                if (col >= L.d_out) continue;
+                float* p = dst + (int64_t)row * d_out + col;
+                *p = (add ? *p : 0.f) + scale * acc[i][j][r];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+__global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems];
+    if (a.status && *a.status) return;
+
+    const DenseSumLayer& L = a.L[blockIdx.z];
+    int tm, tn;
+    if (!tile_of(L, tm, tn)) return;
+    const int m0 = tm * kTM, n0 = tn * kTN;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // w: scalar
+    const int g = lane >> 4, j = lane & 15;
+    const int wm = w & 1, wn = w >> 1;          // wave tile: d_in cols wm*128.., d_out cols wn*64..
+    const int d_in = L.d_in, d_out = L.d_out;
+
+    // Copies per k-step: 16 of A (token rows 2n, 2n + 1 of the 256-column band) and 8 of G
+    // (rows 4n .. 4n + 3 of the 128-column band), 64 lanes x 16 bytes each, landing linearly at
+    // LDS stage + 1 KB * n; wave w issues A copies 4w .. 4w + 3 and G copies 2w, 2w + 1.  A lane
+    // whose chunk lies past d reads column 0 of its row instead: those LDS columns only feed
+    // output columns past d, which are never stored.
+    uint32_t offa[4], offg[2];   // byte offsets from the k-step's first token row
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = 2 * (4 * w + q) + (lane >> 5);
+        const int col = m0 + 8 * ((lane & 31) ^ swz(row));
+        offa[q] = (uint32_t)(row * d_in + (col < d_in ? col : 0)) * 2u;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = 4 * (2 * w + q) + (lane >> 4);
+        const int col = n0 + 8 * ((lane & 15) ^ swz(row));
+        offg[q] = (uint32_t)(row * d_out + (col < d_out ? col : 0)) * 2u;
+    }
+
+    // Transposed operand reads: lane (g, j) points at token row 8g + 4h + j / 4 (h = 0; h = 1 is
+    // 4 rows further), columns 16 blk + 4 (j % 4) .. + 3 of the wave's band.
+    const int sw = 2 * ((j >> 2) | ((g & 1) << 2));    // swz() of those rows
+    const int row0 = 8 * g + (j >> 2);
+    int oa[8], og[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        oa[i] = row0 * kTM + 8 * ((16 * wm + 2 * i + ((j & 3) >> 1)) ^ sw) + 4 * (j & 1);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+        og[jb] = kGOff + row0 * kTN + 8 * ((8 * wn + 2 * jb + ((j & 3) >> 1)) ^ sw) + 4 * (j & 1);
+
+    const int64_t split = blockIdx.y;
+    const int64_t r0 = split * a.rec_per_split;
+    int64_t r1 = r0 + a.rec_per_split;
+    if (r1 > a.n_rec) r1 = a.n_rec;
+    const int nks = (int)(a.T / kTK);
+    const int64_t total = (r1 - r0) * nks;
+    // k-step s covers flat token rows r0 * T + 32 s .. + 31 (T is a multiple of 32)
+    const char* baseA = static_cast<const char*>(L.A) + (r0 * a.T) * (int64_t)d_in * 2;
+    const char* baseG = static_cast<const char*>(L.G) + (r0 * a.T) * (int64_t)d_out * 2;
+    const int64_t strideA = (int64_t)kTK * d_in * 2, strideG = (int64_t)kTK * d_out * 2;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    auto issue = [&](int64_t s, int st) {
+        const char* pa = baseA + s * strideA;
+        const char* pg = baseG + s * strideG;
+        const uint32_t dst = lds0 + (uint32_t)(st * kStageElems) * 2u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) copy16(pa, offa[q], dst + (uint32_t)(4 * w + q) * 1024u);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) copy16(pg, offg[q], dst + (uint32_t)(kGOff * 2 + (2 * w + q) * 1024));
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    float c_cur = 1.f;
+    if (total > 0) {
+        ClipWindow cw;
+        cw.load(a.clip, r0, r1, lane);
+        c_cur = cw.get(a.clip, r0, r1, lane);
+        issue(0, 0);
+        if (total > 1) issue(1, 1);
+        int64_t crec = r0;
+        int cks = 0;
+        int st = 0, st2 = 2;     // stages of steps s and s + 2
+        for (int64_t s = 0; s < total; ++s) {
+            // this wave's copies of step s are done once at most those of step s + 1 (6) are
+            // pending; the barrier then publishes every wave's copies and retires step s - 1,
+            // whose stage the copies of step s + 2 reuse
+            if (s + 1 < total)
+                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (s + 2 < total) issue(s + 2, st2);
+            // record boundary: rescale the accumulator to the new record's factor
+            if (cks == 0 && s > 0) {
+                const float c_new = cw.get(a.clip, crec, r1, lane);
+                const float f = c_cur / c_new;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) acc[i][jb] *= f;
+                c_cur = c_new;
+            }
+            if (++cks == nks) {
+                cks = 0;
+                ++crec;
+            }
+            const uint16_t* S = lds + st * kStageElems;
+            u32x4 bv[4];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const u32x2 lo = tr_read(S + og[jb]);
+                const u32x2 hi = tr_read(S + og[jb] + 4 * kTN);
+                bv[jb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x2 lo = tr_read(S + oa[i]);
+                const u32x2 hi = tr_read(S + oa[i] + 4 * kTM);
+                const u32x4 av = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) acc[i][jb] = mfma_bf16(av, bv[jb], acc[i][jb]);
+            }
+            st = st == 2 ? 0 : st + 1;
+            st2 = st2 == 2 ? 0 : st2 + 1;
+        }
+    }
+    store_tile(L, a.accumulate, split, m0, n0, wm, wn, g, j, c_cur, acc);
+}
 
 __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][kTM * kPitch];
@@ -91,15 +330,9 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
     if (a.status && *a.status) return;
 
     const DenseSumLayer& L = a.L[blockIdx.z];
-    // XCD-aware order: workgroup ids go round-robin over the 8 XCDs; consecutive logical
-    // tiles (same row band of d_in) are gathered on one XCD so that its L2 reuses them.
-    const int n_tiles = L.tiles_m * L.tiles_n;
-    int tile = blockIdx.x;
-    if (n_tiles % 8 == 0) tile = (blockIdx.x % 8) * (n_tiles / 8) + blockIdx.x / 8;
-    if (tile >= n_tiles) return;
-    const int tm = tile / L.tiles_n, tn = tile % L.tiles_n;
+    int tm, tn;
+    if (!tile_of(L, tm, tn)) return;
     const int m0 = tm * kTM, n0 = tn * kTN;
-
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c = lane & 15;
@@ -133,6 +366,8 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
 
     float c_cur = 1.f;
     if (total > 0) {
+        ClipWindow cw;
+        cw.load(a.clip, r0, r1, tid & 63);
         constexpr int D = kDepth;
         u32x4 ring[D][8];
         // (record, k-step) of the next load and of the step being multiplied
@@ -153,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
         if (loads) store_step(stage[0], ld, ring[0]);
         __syncthreads();
 
-        c_cur = a.clip[r0];
+        c_cur = cw.get(a.clip, r0, r1, tid & 63);
         // one k-step: refill the slot step s came from with step s + D, multiply step s
         // out of LDS, stage step s + 1 (slot `next`) into the other LDS buffer.  The loop
         // below is unrolled by D so that every ring slot is a fixed register set.
@@ -163,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
             advance(lrec, lks);
             // record boundary: rescale the accumulator to the new record's factor
             if (cks == 0 && s > 0) {
-                const float c_new = a.clip[crec];
+                const float c_new = cw.get(a.clip, crec, r1, tid & 63);
                 const float f = c_cur / c_new;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
@@ -194,35 +429,23 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
         }
     }
 
-    // epilogue: S = c_last * acc; lane (g, c) holds rows 4g + r, column c of each 16x16 block
-    float* dst = L.out;
-    bool add = a.accumulate != 0;
-    if (L.split_stride) {
-        dst = L.split + split * L.split_stride;
-        add = false;
-    }
-    const int64_t d_out = L.d_out;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * 128 + 16 * i + 4 * g + r;
-            if (row >= L.d_in) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 64 + 16 * j + c;
-                if (col >= L.d_out) continue;
-                float* p = dst + (int64_t)row * d_out + col;
-                *p = (add ? *p : 0.f) + c_cur * acc[i][j][r];
-            }
-        }
-    }
+    store_tile(L, a.accumulate, split, m0, n0, wm, wn, g, c, c_cur, acc);
 }
 
 hipError_t launch_sum_dense(const DenseSumArgs& a, int n_splits, hipStream_t s) {
     int gx = 1;
-    for (int l = 0; l < a.n_layers; ++l) gx = std::max(gx, a.L[l].tiles_m * a.L[l].tiles_n);
-    hipLaunchKernelGGL(k_sum_dense_bf16, dim3(gx, n_splits, a.n_layers), dim3(256), 0, s, a);
+    // the copy kernel needs whole k-steps per record and 16-byte aligned rows (and byte offsets
+    // of 32 token rows that fit 32 bits)
+    bool copy = a.T % kTK == 0;
+    for (int l = 0; l < a.n_layers; ++l) {
+        const DenseSumLayer& d = a.L[l];
+        gx = std::max(gx, d.tiles_m * d.tiles_n);
+        copy = copy && d.vec_a && d.vec_g && d.d_in <= (1 << 24) && d.d_out <= (1 << 24);
+    }
+    if (copy)
+        hipLaunchKernelGGL(k_sum_dense_dma, dim3(gx, n_splits, a.n_layers), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_sum_dense_bf16, dim3(gx, n_splits, a.n_layers), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
