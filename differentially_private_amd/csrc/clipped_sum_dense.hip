@@ -4,22 +4,23 @@
 // Inflation ...", Eq. 3), an MFMA GEMM with M = d_in, N = d_out and the
 // reduction over the n_records * T token rows.
 //
-// Workgroup tile 256 (d_in) x 128 (d_out), 4 wavefronts of 128 x 64 (32
-// v_mfma_f32_16x16x32_bf16 per k-step each), two workgroups per CU, k-step 32
-// tokens.  Both operands are stored with the reduction axis (tokens) as rows, so
-// the MFMA operands (8 consecutive tokens of one column per lane) are a transpose
-// of what memory holds.  Two kernels:
+// Wave tiles are 128 (d_in) x 64 (d_out), 32 v_mfma_f32_16x16x32_bf16 per k-step
+// of 32 tokens.  Both operands are stored with the reduction axis (tokens) as
+// rows, so the MFMA operands (8 consecutive tokens of one column per lane) are a
+// transpose of what memory holds.  Two kernels:
 //
-// k_sum_dense_dma (T a multiple of 32, rows 16-byte aligned): each k-step tile is
-// copied token-major into LDS by global_load_lds_dwordx4 (no registers, no VALU),
-// three LDS stages with loads two k-steps ahead and one barrier per k-step, and
-// the operands come out of LDS through ds_read_b64_tr_b16: within each 16-lane
+// k_sum_dense_dma (T a multiple of 32, rows 16-byte aligned): 256 x 256 workgroup
+// tiles (8 waves, one workgroup per CU).  Each k-step tile is copied token-major
+// into LDS by global_load_lds_dwordx4 (no registers, no VALU), three LDS stages
+// with copies two k-steps ahead and one barrier per k-step, and the operands
+// come out of LDS through ds_read_b64_tr_b16: within each 16-lane
 // group, result lane i element e is element i % 4 of what lane 4e + i / 4 read,
 // so lane 4e + p points at columns 4p..4p+3 of token row e and two such reads give
 // one MFMA operand.  The 16-byte chunk c of token row r sits at chunk c ^ swz(r),
 // which spreads each half-wave's transposed reads over all banks.
 //
-// k_sum_dense_bf16 (any T, any alignment): each k-step is loaded into registers as
+// k_sum_dense_bf16 (any T, any alignment): 256 x 128 workgroup tiles (4 waves, two
+// workgroups per CU); each k-step is loaded into registers as
 // 8 token x 8 column blocks (16-byte loads, zero-filled past T and d), transposed
 // in registers and written as column vectors (pitch 96 bytes: the 16-lane operand
 // reads are conflict-free, the staging writes take 16 cycles), two k-steps of
@@ -91,10 +92,9 @@ __device__ __forceinline__ void store_step(uint16_t* Xs, const Loader& ld, const
     }
 }
 
-constexpr int kStages = 3;                       // LDS stages of the copy kernel
-constexpr int kStageElems = (kTM + kTN) * kTK;   // 12288 bf16 (24 KB): A rows, then G rows
-constexpr int kGOff = kTM * kTK;                 // G part of a stage
-constexpr int kGroupM = 8;                       // tile rows per group of the tile order
+
+constexpr int kCopyTN = 256;     // d_out columns per workgroup of the copy kernel
+constexpr int kCopyStages = 3;   // its LDS stages (4 measured no faster)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -146,29 +146,30 @@ struct ClipWindow {
     }
 };
 
-// Tile of this workgroup.  Workgroup ids go round-robin over the 8 XCDs (ids x, x + 8, ... run
-// on XCD x); those get consecutive logical ids, and logical ids walk groups of kGroupM tile rows
-// column by column, so the ~64 workgroups resident on one XCD cover an 8 x 8 block of tiles and
-// read 8 A column bands and 8 G column bands through that XCD's L2.
-__device__ __forceinline__ bool tile_of(const DenseSumLayer& L, int& tm, int& tn) {
-    const int n_tiles = L.tiles_m * L.tiles_n;
+// Tile of this workgroup among tiles_m x tiles_n.  Workgroup ids go round-robin over the 8 XCDs
+// (ids x, x + 8, ... run on XCD x); those get consecutive logical ids, and logical ids walk groups
+// of group_m tile rows column by column, so the workgroups resident on one XCD cover a compact
+// block of tiles and share their A and G column bands through that XCD's L2.
+__device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    const int n_tiles = tiles_m * tiles_n;
     int t = blockIdx.x;
     if (t >= n_tiles) return false;
     if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
-    const int group = t / (kGroupM * L.tiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(L.tiles_m - first_m, kGroupM);
-    const int r = t - group * kGroupM * L.tiles_n;
+    const int group = t / (group_m * tiles_n);
+    const int first_m = group * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = t - group * group_m * tiles_n;
     tm = first_m + r % gm;
     tn = r / gm;
     return true;
 }
 
-// Writes scale * acc for wave tile (wm, wn); lane (g, c) holds rows 4g + r, column c of each
-// 16 x 16 block.
+// Writes scale * acc for a wave tile of 128 x 16 NB at (m0 + 128 wm, n0 + 16 NB wn); lane (g, c)
+// holds rows 4g + r, column c of each 16 x 16 block.
+template <int NB>
 __device__ __forceinline__ void store_tile(const DenseSumLayer& L, int accumulate, int64_t split,
                                            int m0, int n0, int wm, int wn, int g, int c,
-                                           float scale, const f32x4 (&acc)[8][4]) {
+                                           float scale, const f32x4 (&acc)[8][NB]) {
     float* dst = L.out;
     bool add = accumulate != 0;
     if (L.split_stride) {
@@ -183,8 +184,8 @@ __device__ __forceinline__ void store_tile(const DenseSumLayer& L, int accumulat
             const int row = m0 + wm * 128 + 16 * i + 4 * g + r;
             if (row >= L.d_in) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 64 + 16 * j + c;
+            for (int j = 0; j < NB; ++j) {
+                const int col = n0 + wn * 16 * NB + 16 * j + c;
                 if (col >= L.d_out) continue;
                 float* p = dst + (int64_t)row * d_out + col;
                 *p = (add ? *p : 0.f) + scale * acc[i][j][r];
@@ -195,50 +196,63 @@ __device__ __forceinline__ void store_tile(const DenseSumLayer& L, int accumulat
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems];
+// 256 x 256 workgroup tiles, 8 wavefronts of 128 x 64, 3 LDS stages of 32 KB (copies run two
+// k-steps ahead), one workgroup per CU.
+__global__ __launch_bounds__(512, 1) void k_sum_dense_dma(DenseSumArgs a) {
+    constexpr int TN = kCopyTN;                     // d_out columns per workgroup
+    constexpr int WN = 64;                          // d_out columns per wave
+    constexpr int NS = kCopyStages;
+    constexpr int W = 2 * TN / WN;                  // wavefronts
+    constexpr int NB = WN / 16;                     // 16-column G blocks per wave
+    constexpr int kStageElems = (kTM + TN) * kTK;   // A rows (256 columns), then G rows (TN)
+    constexpr int kGOff = kTM * kTK;
+    constexpr int CA = 16 / W;                      // A copies per wave per k-step
+    constexpr int CG = (TN / 16) / W;               // G copies per wave per k-step
+    constexpr int kRowsG = 1024 / (TN * 2);         // token rows per G copy
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NS * kStageElems];
     if (a.status && *a.status) return;
 
     const DenseSumLayer& L = a.L[blockIdx.z];
+    const int d_in = L.d_in, d_out = L.d_out;
     int tm, tn;
-    if (!tile_of(L, tm, tn)) return;
-    const int m0 = tm * kTM, n0 = tn * kTN;
+    if (!tile_of((d_in + kTM - 1) / kTM, (d_out + TN - 1) / TN, TN == 128 ? 8 : 4, tm, tn)) return;
+    const int m0 = tm * kTM, n0 = tn * TN;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // w: scalar
     const int g = lane >> 4, j = lane & 15;
-    const int wm = w & 1, wn = w >> 1;          // wave tile: d_in cols wm*128.., d_out cols wn*64..
-    const int d_in = L.d_in, d_out = L.d_out;
+    const int wm = w & 1, wn = w >> 1;          // wave tile: d_in cols wm*128.., d_out cols wn*WN..
 
-    // Copies per k-step: 16 of A (token rows 2n, 2n + 1 of the 256-column band) and 8 of G
-    // (rows 4n .. 4n + 3 of the 128-column band), 64 lanes x 16 bytes each, landing linearly at
-    // LDS stage + 1 KB * n; wave w issues A copies 4w .. 4w + 3 and G copies 2w, 2w + 1.  A lane
-    // whose chunk lies past d reads column 0 of its row instead: those LDS columns only feed
-    // output columns past d, which are never stored.
-    uint32_t offa[4], offg[2];   // byte offsets from the k-step's first token row
+    // Copies per k-step: 16 of A (token rows 2n, 2n + 1 of the 256-column band) and TN / 16 of G
+    // (kRowsG token rows each), 64 lanes x 16 bytes each, landing linearly at LDS stage + 1 KB * n;
+    // wave w issues A copies CA w .. CA w + CA - 1 and G copies CG w .. CG w + CG - 1.  A lane whose
+    // chunk lies past d reads column 0 of its row instead: those LDS columns only feed output
+    // columns past d, which are never stored.
+    uint32_t offa[CA], offg[CG];   // byte offsets from the k-step's first token row
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int row = 2 * (4 * w + q) + (lane >> 5);
+    for (int q = 0; q < CA; ++q) {
+        const int row = 2 * (CA * w + q) + (lane >> 5);
         const int col = m0 + 8 * ((lane & 31) ^ swz(row));
         offa[q] = (uint32_t)(row * d_in + (col < d_in ? col : 0)) * 2u;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = 4 * (2 * w + q) + (lane >> 4);
-        const int col = n0 + 8 * ((lane & 15) ^ swz(row));
+    for (int q = 0; q < CG; ++q) {
+        const int row = kRowsG * (CG * w + q) + lane / (64 / kRowsG);
+        const int col = n0 + 8 * ((lane % (64 / kRowsG)) ^ swz(row));
         offg[q] = (uint32_t)(row * d_out + (col < d_out ? col : 0)) * 2u;
     }
 
     // Transposed operand reads: lane (g, j) points at token row 8g + 4h + j / 4 (h = 0; h = 1 is
-    // 4 rows further), columns 16 blk + 4 (j % 4) .. + 3 of the wave's band.
+    // 4 rows further), columns 16 blk + 4 (j % 4) .. + 3 of the wave's band, i.e. chunk
+    // c = 16 wm + 2 blk + (j % 4) / 2 (A) or (WN / 8) wn + 2 blk + (j % 4) / 2 (G), stored at c ^ sw.
     const int sw = 2 * ((j >> 2) | ((g & 1) << 2));    // swz() of those rows
     const int row0 = 8 * g + (j >> 2);
-    int oa[8], og[4];
+    int oa[8], og[NB];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         oa[i] = row0 * kTM + 8 * ((16 * wm + 2 * i + ((j & 3) >> 1)) ^ sw) + 4 * (j & 1);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-        og[jb] = kGOff + row0 * kTN + 8 * ((8 * wn + 2 * jb + ((j & 3) >> 1)) ^ sw) + 4 * (j & 1);
+    for (int jb = 0; jb < NB; ++jb)
+        og[jb] = kGOff + row0 * TN + 8 * (((WN / 8) * wn + 2 * jb + ((j & 3) >> 1)) ^ sw) + 4 * (j & 1);
 
     const int64_t split = blockIdx.y;
     const int64_t r0 = split * a.rec_per_split;
@@ -256,37 +270,51 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
         const char* pg = baseG + s * strideG;
         const uint32_t dst = lds0 + (uint32_t)(st * kStageElems) * 2u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) copy16(pa, offa[q], dst + (uint32_t)(4 * w + q) * 1024u);
+        for (int q = 0; q < CA; ++q) copy16(pa, offa[q], dst + (uint32_t)(CA * w + q) * 1024u);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) copy16(pg, offg[q], dst + (uint32_t)(kGOff * 2 + (2 * w + q) * 1024));
+        for (int q = 0; q < CG; ++q)
+            copy16(pg, offg[q], dst + (uint32_t)(kGOff * 2 + (CG * w + q) * 1024));
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[8][NB];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jb = 0; jb < NB; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Wait until this wave's copies of step t are done, given that steps up to `last` have been
+    // issued (their copies may stay in flight: vmcnt counts this wave's outstanding copies, which
+    // complete in issue order); the barrier then publishes every wave's copies of step t.
+    static_assert(NS >= 2 && NS <= 5, "vmcnt cases");
+    auto wait_step = [&](int64_t t, int64_t last) {
+        const int64_t later = last - t;
+        if (later >= 3)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (CA + CG)) : "memory");
+        else if (later == 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (CA + CG)) : "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CA + CG) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
 
     float c_cur = 1.f;
     if (total > 0) {
         ClipWindow cw;
         cw.load(a.clip, r0, r1, lane);
         c_cur = cw.get(a.clip, r0, r1, lane);
-        issue(0, 0);
-        if (total > 1) issue(1, 1);
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k)
+            if (k < total) issue(k, k);
         int64_t crec = r0;
         int cks = 0;
-        int st = 0, st2 = 2;     // stages of steps s and s + 2
+        int st = 0, stn = NS - 1;     // stages of steps s and s + NS - 1
         for (int64_t s = 0; s < total; ++s) {
-            // this wave's copies of step s are done once at most those of step s + 1 (6) are
-            // pending; the barrier then publishes every wave's copies and retires step s - 1,
-            // whose stage the copies of step s + 2 reuse
-            if (s + 1 < total)
-                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (s + 2 < total) issue(s + 2, st2);
+            // publish step s; the barrier also retires step s - 1, whose stage the copies of step
+            // s + NS - 1 reuse
+            wait_step(s, min<int64_t>(s + NS - 2, total - 1));
+            if (s + NS - 1 < total) issue(s + NS - 1, stn);
             // record boundary: rescale the accumulator to the new record's factor
             if (cks == 0 && s > 0) {
                 const float c_new = cw.get(a.clip, crec, r1, lane);
@@ -294,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb) acc[i][jb] *= f;
+                    for (int jb = 0; jb < NB; ++jb) acc[i][jb] *= f;
                 c_cur = c_new;
             }
             if (++cks == nks) {
@@ -302,11 +330,11 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
                 ++crec;
             }
             const uint16_t* S = lds + st * kStageElems;
-            u32x4 bv[4];
+            u32x4 bv[NB];
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
+            for (int jb = 0; jb < NB; ++jb) {
                 const u32x2 lo = tr_read(S + og[jb]);
-                const u32x2 hi = tr_read(S + og[jb] + 4 * kTN);
+                const u32x2 hi = tr_read(S + og[jb] + 4 * TN);
                 bv[jb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
@@ -315,10 +343,10 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_dma(DenseSumArgs a) {
                 const u32x2 hi = tr_read(S + oa[i] + 4 * kTM);
                 const u32x4 av = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) acc[i][jb] = mfma_bf16(av, bv[jb], acc[i][jb]);
+                for (int jb = 0; jb < NB; ++jb) acc[i][jb] = mfma_bf16(av, bv[jb], acc[i][jb]);
             }
-            st = st == 2 ? 0 : st + 1;
-            st2 = st2 == 2 ? 0 : st2 + 1;
+            st = st == NS - 1 ? 0 : st + 1;
+            stn = stn == NS - 1 ? 0 : stn + 1;
         }
     }
     store_tile(L, a.accumulate, split, m0, n0, wm, wn, g, j, c_cur, acc);
@@ -331,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void k_sum_dense_bf16(DenseSumArgs a) {
 
     const DenseSumLayer& L = a.L[blockIdx.z];
     int tm, tn;
-    if (!tile_of(L, tm, tn)) return;
+    if (!tile_of(L.tiles_m, L.tiles_n, 8, tm, tn)) return;
     const int m0 = tm * kTM, n0 = tn * kTN;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
@@ -442,8 +470,12 @@ hipError_t launch_sum_dense(const DenseSumArgs& a, int n_splits, hipStream_t s) 
         gx = std::max(gx, d.tiles_m * d.tiles_n);
         copy = copy && d.vec_a && d.vec_g && d.d_in <= (1 << 24) && d.d_out <= (1 << 24);
     }
-    if (copy)
-        hipLaunchKernelGGL(k_sum_dense_dma, dim3(gx, n_splits, a.n_layers), dim3(256), 0, s, a);
+    if (copy) {
+        int gxc = 1;
+        for (int l = 0; l < a.n_layers; ++l)
+            gxc = std::max(gxc, ((a.L[l].d_in + kTM - 1) / kTM) * ((a.L[l].d_out + kCopyTN - 1) / kCopyTN));
+        hipLaunchKernelGGL(k_sum_dense_dma, dim3(gxc, n_splits, a.n_layers), dim3(2 * kCopyTN), 0, s, a);
+    }
     else
         hipLaunchKernelGGL(k_sum_dense_bf16, dim3(gx, n_splits, a.n_layers), dim3(256), 0, s, a);
     return hipGetLastError();

@@ -70,7 +70,7 @@ struct LayerPlan {
     int64_t n_parts, part_off;
     int64_t stored_off;  // bytes into ws (STORED)
     int64_t split_off;   // bytes into ws (GEMM with splits)
-    bool dense;          // GEMM sum on the 256x128-tile dense kernel (bf16, both dimensions > 16)
+    bool dense;          // GEMM sum on the dense MFMA kernels (bf16, both dimensions > 16)
 };
 
 struct dpsgd_plan {
@@ -294,7 +294,7 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
     }
     if (n_rec == 0) return DPSGD_OK;
 
-    // 2) dense GEMM layers (bf16): 256x128-tile MFMA kernel, split over records
+    // 2) dense GEMM layers (bf16): MFMA GEMM kernels, split over records
     {
         int nsd = (int)std::min<int64_t>(p->n_splits_dense_max, n_rec);
         const int64_t rpsd = (n_rec + nsd - 1) / nsd;
@@ -580,13 +580,13 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     }
 
     // split counts of the GEMM clipped sums: ~8192 wavefronts per launch for the tile
-    // engine, >= 512 workgroups (two per CU) for the dense kernel (256 x 128 tiles)
+    // engine, >= 256 workgroups of 256 x 256 tiles (one per CU) for the dense kernels
     int64_t waves = 0, dense_wgs = 0;
     for (LayerPlan& lp : p->layers) {
         if (lp.sum_mode != DPSGD_SUM_GEMM) continue;
         lp.dense = p->dtype == DPSGD_DTYPE_BF16 && lp.tiles.mb == 2;
         if (lp.dense)
-            dense_wgs += ((lp.d_in + 255) / 256) * ((lp.d_out + 127) / 128);
+            dense_wgs += ((lp.d_in + 255) / 256) * ((lp.d_out + 255) / 256);
         else
             waves += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
     }
@@ -596,7 +596,7 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
                                       std::max<int64_t>(1, (target + units - 1) / units));
     };
     const int ns = splits_for(waves, 8192);
-    const int nsd = splits_for(dense_wgs, 512);
+    const int nsd = splits_for(dense_wgs, 256);
     p->n_splits_max = ns;
     p->n_splits_dense_max = nsd;
 
