@@ -104,25 +104,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // each) then fall on 16 distinct chunk slots of the 256-byte bank space.
 __device__ __forceinline__ int swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
 
-// LDS byte address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// global_load_lds_dwordx4: 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
-// Written out so that the compiler does not track it as an LDS store: it would otherwise wait
-// for every copy in flight (vmcnt(0)) before each LDS read and barrier, since it cannot tell
-// the stages apart.  Completion is awaited explicitly (vmcnt) before the barrier that
-// publishes a stage.
-__device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t lds) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(base), "s"(lds)
-        : "memory", "m0");
-}
-
 __device__ __forceinline__ u32x2 tr_read(const uint16_t* l) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(l));
@@ -283,19 +264,10 @@ __global__ __launch_bounds__(512, 1) void k_sum_dense_dma(DenseSumArgs a) {
         for (int jb = 0; jb < NB; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Wait until this wave's copies of step t are done, given that steps up to `last` have been
-    // issued (their copies may stay in flight: vmcnt counts this wave's outstanding copies, which
-    // complete in issue order); the barrier then publishes every wave's copies of step t.
-    static_assert(NS >= 2 && NS <= 5, "vmcnt cases");
+    // issued (later ones may stay in flight); the barrier then publishes every wave's copies.
+    static_assert(NS >= 2 && NS <= 5, "stages");
     auto wait_step = [&](int64_t t, int64_t last) {
-        const int64_t later = last - t;
-        if (later >= 3)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (CA + CG)) : "memory");
-        else if (later == 2)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (CA + CG)) : "memory");
-        else if (later == 1)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CA + CG) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_copies<CA + CG>(last - t);
         __syncthreads();
     };
 

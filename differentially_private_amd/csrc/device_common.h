@@ -75,6 +75,40 @@ __device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts,
     for (int j = 0; j < 4; ++j) out[j] = wave_sum_d(s[j]);
 }
 
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
+// Written out so that the compiler does not track it as an LDS store: it would otherwise wait
+// for every copy in flight (vmcnt(0)) before each LDS read and barrier, since it cannot tell
+// the stages of a multi-stage pipeline apart.  Callers await completion explicitly (vmcnt)
+// before the barrier that publishes a stage; base and lds must be wave-uniform.
+__device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(min(later, 3) * PER): wait until at most the `later` most recently issued
+// k-steps of PER copies each are still in flight (copies complete in issue order).
+template <int PER>
+__device__ __forceinline__ void wait_copies(int64_t later) {
+    static_assert(3 * PER <= 63, "vmcnt range");
+    if (later >= 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+    else if (later == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+    else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of the A block and
 // column (l % 16) of the B block, each with 8 consecutive k of group l / 16;
 // the 16x16 fp32 result has column l % 16, rows 4 * (l / 16) + {0..3} in lane l.

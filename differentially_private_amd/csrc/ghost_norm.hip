@@ -172,6 +172,148 @@ __global__ __launch_bounds__(256) void k_norm_gram(GramArgs args) {
         args.parts[rec * args.parts_stride + L.part_off + pair] = (tb == sb) ? s : 2.f * s;
 }
 
+// ---- Gram path, bf16 inputs with 16-byte aligned rows and d_in, d_out multiples of 32 ----
+//
+// One workgroup (4 waves) per (record, layer, 128-token block pair I <= J).  Wave (wm, wn) owns
+// the 64 x 64 sub-pair (2I + wm, 2J + wn) of the 64-token block grid and writes the partial of
+// that sub-pair to the same slot k_norm_gram uses: the Gram blocks of A and of G over all
+// features, then the sum of their Hadamard product, doubled off the diagonal.  In a diagonal
+// workgroup wave (1, 0) holds the mirror image of wave (0, 1)'s sub-pair and writes nothing.
+//
+// Features stream in k-steps of 32 through one copy pipeline, first A's d_in features, then G's
+// d_out: per k-step the 128 I rows and 128 J rows (16 blocks of 16 rows, 16 KB) are copied by
+// global_load_lds_dwordx4 into 3 LDS stages, two k-steps ahead, one barrier per k-step.  Each
+// 16-row block is stored chunk-major (8-feature chunk k of row r at byte 256 k + 16 r), so an
+// MFMA operand read (lane 16 g + c: row c, chunk g) is one linear 16-byte-per-lane LDS read.
+// Token rows past T are copied from row T - 1 and left out of the Hadamard sum.
+constexpr int kGramB = 128;                   // tokens per block
+constexpr int kGramK = 32;                    // features per k-step
+constexpr int kGramStages = 3;
+constexpr int kGramStage = 2 * kGramB * kGramK * 2;   // 16 KB: I rows, then J rows
+
+__global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kGramStages * kGramStage / 2];
+    const GramLayer& L = args.L[blockIdx.z];
+    const int nb = (int)((args.T + kGramB - 1) / kGramB);
+    const int np = nb * (nb + 1) / 2;
+    // workgroup -> (record, pair): workgroup ids go round-robin over the 8 XCDs and the pairs
+    // of one record get ids equal mod 8, so they share an XCD's L2
+    const int x = blockIdx.x;
+    const int q = x >> 3;
+    const int pair = q % np;
+    const int64_t rec = 8 * (int64_t)(q / np) + (x & 7);
+    if (rec >= args.n_rec) return;
+    int I = 0, rem = pair;
+    while (rem >= nb - I) {
+        rem -= nb - I;
+        ++I;
+    }
+    const int J = I + rem;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // w: scalar
+    const int g = lane >> 4, c = lane & 15;
+    const int wm = w & 1, wn = w >> 1;
+    const int64_t T = args.T;
+    const int tb = 2 * I + wm, sb = 2 * J + wn;          // 64-token sub-blocks of this wave
+    const bool mirror = (I == J) && wm > wn;
+    const bool active = !mirror && tb < args.nb && sb < args.nb;
+
+    // copies: blocks 0..7 are I rows 16 b .., blocks 8..15 J rows; wave w issues blocks 4w .. 4w+3;
+    // lane L fetches chunk L / 16 of row L % 16 (row clamped to T - 1)
+    uint32_t offa[4], offg[4];   // byte offsets from the record's row 0 at the k-step's features
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = 4 * w + k;
+        int64_t t = (b < 8 ? (int64_t)I * kGramB + 16 * b : (int64_t)J * kGramB + 16 * (b - 8)) + (lane & 15);
+        if (t > T - 1) t = T - 1;
+        offa[k] = (uint32_t)((t * L.d_in + 8 * (lane >> 4)) * 2);
+        offg[k] = (uint32_t)((t * L.d_out + 8 * (lane >> 4)) * 2);
+    }
+    const int nA = L.d_in / kGramK, nG = L.d_out / kGramK;
+    const int total = nA + nG;
+    const char* recA = static_cast<const char*>(L.A) + rec * T * L.d_in * 2;
+    const char* recG = static_cast<const char*>(L.G) + rec * T * L.d_out * 2;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    auto issue = [&](int s, int st) {
+        const uint32_t dst = lds0 + (uint32_t)(st * kGramStage + 4 * w * 1024);
+        if (s < nA) {
+            const char* base = recA + (int64_t)s * kGramK * 2;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) copy16(base, offa[k], dst + k * 1024);
+        } else {
+            const char* base = recG + (int64_t)(s - nA) * kGramK * 2;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) copy16(base, offg[k], dst + k * 1024);
+        }
+    };
+
+    f32x4 ga[4][4], gg[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            ga[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gg[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+#pragma unroll
+    for (int k = 0; k < kGramStages - 1; ++k)
+        if (k < total) issue(k, k);
+    int st = 0, stn = kGramStages - 1;
+    for (int s = 0; s < total; ++s) {
+        // publish step s (this wave's copies done, later ones may stay in flight); the barrier
+        // also retires step s - 1, whose stage the copies of step s + 2 reuse
+        wait_copies<4>(min(s + kGramStages - 2, total - 1) - s);
+        __syncthreads();
+        if (s + kGramStages - 1 < total) issue(s + kGramStages - 1, stn);
+        if (active) {
+            const uint16_t* S = lds + st * (kGramStage / 2);
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * wm + mi) * 512 + 8 * lane);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                bv[ni] = *reinterpret_cast<const u32x4*>(S + (8 + 4 * wn + ni) * 512 + 8 * lane);
+            if (s < nA) {
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) ga[mi][ni] = mfma_bf16(av[mi], bv[ni], ga[mi][ni]);
+            } else {
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) gg[mi][ni] = mfma_bf16(av[mi], bv[ni], gg[mi][ni]);
+            }
+        }
+        st = st == kGramStages - 1 ? 0 : st + 1;
+        stn = stn == kGramStages - 1 ? 0 : stn + 1;
+    }
+
+    // Hadamard sum over this wave's valid entries: lane (g, c) holds rows 4g + r, column c of
+    // each 16 x 16 block
+    float sum = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = (int64_t)64 * tb + 16 * mi + 4 * g + r;
+                const int64_t u = (int64_t)64 * sb + 16 * ni + c;
+                const float v = ga[mi][ni][r] * gg[mi][ni][r];
+                sum += (t < T && u < T) ? v : 0.f;
+            }
+    sum = wave_sum(sum);
+    if (active && lane == 0) {
+        const int nb64 = args.nb;
+        const int p64 = tb * nb64 - tb * (tb - 1) / 2 + (sb - tb);
+        args.parts[rec * args.parts_stride + L.part_off + p64] = (tb == sb) ? sum : 2.f * sum;
+    }
+}
+
 hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s) {
     int gx = 1;
     for (int l = 0; l < a.n_layers; ++l) {
@@ -192,6 +334,20 @@ hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store
 }
 
 hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s) {
+    // the copy kernel: bf16, rows 16-byte aligned, whole k-steps of features, and byte offsets
+    // within a record below 2^31
+    bool copy = dtype == kBF16 && a.n_rec > 0;
+    for (int l = 0; l < a.n_layers; ++l) {
+        const GramLayer& d = a.L[l];
+        copy = copy && d.vec_a && d.vec_g && d.d_in % kGramK == 0 && d.d_out % kGramK == 0 &&
+               a.T * (int64_t)std::max(d.d_in, d.d_out) * 2 < ((int64_t)1 << 31);
+    }
+    if (copy) {
+        const int64_t nb = (a.T + kGramB - 1) / kGramB;
+        const int64_t gx = nb * (nb + 1) / 2 * 8 * ((a.n_rec + 7) / 8);
+        hipLaunchKernelGGL(k_norm_gram_copy, dim3((unsigned)gx, 1, a.n_layers), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid((a.n_pairs + 3) / 4, (unsigned)a.n_rec, a.n_layers);
     if (dtype == kBF16)
         hipLaunchKernelGGL(k_norm_gram<kBF16>, grid, dim3(256), 0, s, a);
