@@ -108,6 +108,19 @@ def cpu_baseline(w, seconds):
                       f"noise included, input generation excluded), {el:.1f} s wall"}
 
 
+def sum_roofline(work, w, phase):
+    """Algorithmic rate of the clipped-sum phase when it was timed alone (GEMM strategy: flops
+    against the bf16/fp32 MFMA peak; STORED: bytes against HBM)."""
+    if "clipped_sum" not in phase:
+        return None
+    sb, sf = work["clipped_sum"]
+    t = phase["clipped_sum"] * 1e-3
+    if sf:
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        return {"TFLOPs": sf * w.n_phys / t / 1e12, "mfma_frac": sf * w.n_phys / t / 1e12 / peak}
+    return {"hbm_GBps": sb * w.n_phys / t / 1e9, "hbm_frac": sb * w.n_phys / t / 1e9 / HBM_PEAK_GBS}
+
+
 def secondary(args, w, torch, dev, dp, datagen):
     """Secondary lines for workloads 1, 3, 4, 5: one step = all physical batches of a logical
     batch (virtual batching: norms/clip/sum per physical batch, noise once), inputs resident in
@@ -145,13 +158,21 @@ def secondary(args, w, torch, dev, dp, datagen):
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / args.steps
         As, Gs = batches[0]
-        x0, x1 = ev(), ev()
-        x0.record(stream)
-        for _ in range(args.steps):
-            dp.norms(plan, w.B, 0, L, As, Gs, ws)
-        x1.record(stream)
-        torch.cuda.synchronize()
-        phase["norms"] = x0.elapsed_time(x1) / args.steps * w.n_phys
+
+        def timed(fn):
+            x0, x1 = ev(), ev()
+            x0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            x1.record(stream)
+            torch.cuda.synchronize()
+            return x0.elapsed_time(x1) / args.steps
+        # each phase alone on physical batch 0 (K back-to-back calls between HIP events)
+        phase["norms"] = timed(lambda: dp.norms(plan, w.B, 0, L, As, Gs, ws)) * w.n_phys
+        phase["clip"] = timed(lambda: dp.clip(plan, w.B, w.C, ws)) * w.n_phys
+        phase["clipped_sum"] = timed(
+            lambda: dp.clipped_sum(plan, w.B, 0, L, As, Gs, None, out, ws)) * w.n_phys
+        phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws))
         phase["finish"] = ms - phase["norms"]
     else:
         # layer-chunk streaming: chunks of inputs filled (untimed), norms timed per chunk
@@ -210,6 +231,7 @@ def secondary(args, w, torch, dev, dp, datagen):
             "norms_roofline": {"hbm_GBps": nb / (phase["norms"] * 1e-3) / 1e9,
                                "hbm_frac": nb / (phase["norms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "TFLOPs": nf / (phase["norms"] * 1e-3) / 1e12},
+            "clipped_sum_roofline": sum_roofline(work, w, phase),
             "finish_bytes": work["clipped_sum"][0] * (w.n_phys if work["clipped_sum"][1] else 1)}
     print(json.dumps(line), flush=True)
 
