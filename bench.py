@@ -136,7 +136,7 @@ def secondary(args, w, torch, dev, dp, datagen):
     free = torch.cuda.mem_get_info()[0]
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    phase = {"norms": 0.0, "finish": 0.0}
+    phase = {"norms": 0.0, "rest_of_step": 0.0}
     note = ""
     if w.n_phys * in_bytes < free - (8 << 30):
         batches = [device_inputs(w, datagen, torch, dev, p * w.B, w.B) for p in range(w.n_phys)]
@@ -173,7 +173,7 @@ def secondary(args, w, torch, dev, dp, datagen):
         phase["clipped_sum"] = timed(
             lambda: dp.clipped_sum(plan, w.B, 0, L, As, Gs, None, out, ws)) * w.n_phys
         phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws))
-        phase["finish"] = ms - phase["norms"]
+        phase["rest_of_step"] = ms - phase["norms"]   # residual: the step minus the norms timed alone
     else:
         # layer-chunk streaming: chunks of inputs filled (untimed), norms timed per chunk
         note = "layer-chunk streaming, staging excluded"
@@ -213,8 +213,8 @@ def secondary(args, w, torch, dev, dp, datagen):
         y1.record(stream)
         torch.cuda.synchronize()
         phase["norms"] = ms_norm
-        phase["finish"] = y0.elapsed_time(y1) / args.steps
-        ms = ms_norm + phase["finish"]
+        phase["rest_of_step"] = y0.elapsed_time(y1) / args.steps
+        ms = ms_norm + phase["rest_of_step"]
     assert dp.status(plan, ws) == dp.OK
     work = algorithmic_work(w, plan, dp)
     nb, nf = work["norms"]
@@ -232,7 +232,7 @@ def secondary(args, w, torch, dev, dp, datagen):
                                "hbm_frac": nb / (phase["norms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "TFLOPs": nf / (phase["norms"] * 1e-3) / 1e12},
             "clipped_sum_roofline": sum_roofline(work, w, phase),
-            "finish_bytes": work["clipped_sum"][0] * (w.n_phys if work["clipped_sum"][1] else 1)}
+            "clipped_sum_bytes": work["clipped_sum"][0] * w.n_phys}
     print(json.dumps(line), flush=True)
 
 
