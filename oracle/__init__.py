@@ -178,13 +178,23 @@ def add_noise(S_flat: np.ndarray, first_e: int, sigma: float, C: float, seed: in
     return S_flat
 
 
+def descent(theta, g_noised, lr: float, normalizer: float):
+    """Phase 5 of the step ("Privacy-Preserving Machine Learning", section "Differentially
+    private stochastic gradient descent", the descent step): the noised sum is divided by the
+    fixed public normaliser L, scaled by the learning rate and subtracted from the parameters,
+    theta' = theta - lr * (g_noised / L).  float64 in and out."""
+    return np.asarray(theta, dtype=np.float64) - lr * (np.asarray(g_noised, dtype=np.float64) / normalizer)
+
+
 def step(layers_A, layers_G, C: float, sigma: float, seed: int, step_idx: int,
-         noise: bool = True, batches=None):
+         noise: bool = True, batches=None, descent_args=None):
     """Whole step for inputs given per layer (lists of [B,T,d] arrays).  `batches` optionally
     lists physical batches as (layers_A, layers_G) tuples for virtual batching: norms and clip
     factors are per physical batch (each record only ever sees its own data), the clipped sums
-    accumulate across batches, and noise is drawn once.  Returns dict with n, c (concatenated
-    over batches in logical record order), S (list per layer, pre-noise), S_noised (list)."""
+    accumulate across batches, and noise is drawn once.  `descent_args` = (thetas per layer, lr,
+    L) adds the descent step on the noised sum (it is part of the release, so it needs the
+    noise).  Returns dict with n, c (concatenated over batches in logical record order), S (list
+    per layer, pre-noise), S_noised (list) and, with descent_args, theta (list)."""
     if batches is None:
         batches = [(layers_A, layers_G)]
     L = len(batches[0][0])
@@ -209,4 +219,10 @@ def step(layers_A, layers_G, C: float, sigma: float, seed: int, step_idx: int,
     for s in shapes:
         out.append(noised[off:off + s[0] * s[1]].reshape(s))
         off += s[0] * s[1]
-    return {"n": np.concatenate(ns), "c": np.concatenate(cs), "S": S, "S_noised": out}
+    res = {"n": np.concatenate(ns), "c": np.concatenate(cs), "S": S, "S_noised": out}
+    if descent_args is not None:
+        if not noise:
+            raise ValueError("the descent step releases the noised sum: it needs the noise")
+        thetas, lr, L = descent_args
+        res["theta"] = [descent(t, o, lr, L) for t, o in zip(thetas, out)]
+    return res

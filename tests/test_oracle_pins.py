@@ -372,3 +372,34 @@ def test_noise_added_to_every_coordinate():
     pre = np.concatenate([s.reshape(-1) for s in r["S"]])
     assert np.all(flat != pre)
     np.testing.assert_allclose(flat - pre, oracle.gauss(0, 0, 0, flat.size), rtol=1e-14, atol=1e-15)
+
+
+def test_descent_worked_example(golden_dir):
+    """Phase 5 on the page's clip_vector_l2 example (no noise): theta1 worked by hand from the
+    printed clipped sum [1.60, 1.90] with eta = 0.5, L = 2."""
+    g = json.load(open(os.path.join(golden_dir, "p1_clip_example.json")))
+    d = json.load(open(os.path.join(golden_dir, "p1_descent_example.json")))
+    grads = np.array(g["gradients"], dtype=np.float64)
+    A = [np.ones((len(grads), 1, 1))]
+    G = [grads.reshape(len(grads), 1, 2)]
+    theta0 = [np.array(d["theta0"], dtype=np.float64).reshape(1, 2)]
+    r = oracle.step(A, G, g["C"], 0.0, 0, 0, descent_args=(theta0, d["learning_rate"], d["normalizer"]))
+    assert np.allclose(r["theta"][0].reshape(-1), d["theta1"], rtol=0, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.step(A, G, g["C"], 0.0, 0, 0, noise=False, descent_args=(theta0, 0.5, 2.0))
+
+
+def test_descent_step_noise_rms_page(golden_dir):
+    """A pure-noise step (empty batch) from theta0 = 0 over d = 5e6 coordinates with the page's
+    sigma*C = 1, eta = 0.01, L = 128: the step's norm is the page's step-noise RMS 0.17, within
+    5 standard deviations of eta*sigma*C*||Z||/L around eta*sigma*C*sqrt(d)/L."""
+    g = json.load(open(os.path.join(golden_dir, "p1_noise_rms.json")))
+    d = g["d_adapter"]
+    di, do = 5000, d // 5000
+    A = [np.zeros((0, 1, di))]
+    G = [np.zeros((0, 1, do))]
+    lr, L = g["learning_rate"], g["normalizer"]
+    r = oracle.step(A, G, 1.0, g["sigma_c"], 0, 0, descent_args=([np.zeros((di, do))], lr, L))
+    step_norm = np.linalg.norm(r["theta"][0])
+    assert round(step_norm, 2) == g["adapter_step_rms_2dp"]
+    assert abs(step_norm - lr * g["sigma_c"] * math.sqrt(d) / L) < 5 * lr / (L * math.sqrt(2))
