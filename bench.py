@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "records/sec per DP-SGD clip+noise step; % MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0
+DESCENT_LR, DESCENT_L = 0.01, 1.0   # --descent: the sensitivity paper's release audit settings
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0}   # dense fp32 / bf16 MFMA
 
 
@@ -131,6 +132,8 @@ def secondary(args, w, torch, dev, dp, datagen):
     plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
     ws = plan.workspace(dev)
     out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+    theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+             if args.descent else None)
     e = 4 if w.dtype == 0 else 2
     in_bytes = w.input_bytes_per_batch()
     free = torch.cuda.mem_get_info()[0]
@@ -144,9 +147,12 @@ def secondary(args, w, torch, dev, dp, datagen):
         def step():
             for p, (As, Gs) in enumerate(batches):
                 flags = (dp.NO_NOISE if w.n_phys > 1 else 0) | (dp.ACCUMULATE if p else 0)
-                dp.step(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, flags=flags)
+                last = w.n_phys == 1
+                dp.step(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, flags=flags,
+                        params=theta if last else None, lr=DESCENT_LR, normalizer=DESCENT_L)
             if w.n_phys > 1:
-                dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws)
+                dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws, params=theta,
+                         lr=DESCENT_LR, normalizer=DESCENT_L)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -172,7 +178,8 @@ def secondary(args, w, torch, dev, dp, datagen):
         phase["clip"] = timed(lambda: dp.clip(plan, w.B, w.C, ws)) * w.n_phys
         phase["clipped_sum"] = timed(
             lambda: dp.clipped_sum(plan, w.B, 0, L, As, Gs, None, out, ws)) * w.n_phys
-        phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws))
+        phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws,
+                                                params=theta, lr=DESCENT_LR, normalizer=DESCENT_L))
         phase["rest_of_step"] = ms - phase["norms"]   # residual: the step minus the norms timed alone
     else:
         # layer-chunk streaming: chunks of inputs filled (untimed), norms timed per chunk
@@ -209,7 +216,8 @@ def secondary(args, w, torch, dev, dp, datagen):
         for _ in range(args.steps):
             dp.clip(plan, w.B, w.C, ws)
             dp.clipped_sum(plan, w.B, 0, L, None, None, None, out, ws)
-            dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws)
+            dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws, params=theta, lr=DESCENT_LR,
+                     normalizer=DESCENT_L)
         y1.record(stream)
         torch.cuda.synchronize()
         phase["norms"] = ms_norm
@@ -226,7 +234,8 @@ def secondary(args, w, torch, dev, dp, datagen):
             "data": "synthetic",
             "config": {"workload": w.name, "layers": L, "params": w.n_params,
                        "records_per_step": w.logical_B, "physical_batches": w.n_phys, "tokens": w.T,
-                       "parallelism": "single GPU", "note": note},
+                       "parallelism": "single GPU", "note": note,
+                       "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
             "phases_ms": phase,
             "norms_roofline": {"hbm_GBps": nb / (phase["norms"] * 1e-3) / 1e9,
                                "hbm_frac": nb / (phase["norms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -254,6 +263,9 @@ def main():
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB "
                          "(the reference for scaling HBM byte counters)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--descent", action="store_true",
+                    help="fuse the descent step theta -= lr * noised sum / L into the timed step, with "
+                         "lr 0.01 and L 1 (the sensitivity paper's release audit settings)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -303,7 +315,10 @@ def main():
                           "algorithmic_bytes": algorithmic_work(w, plan, dp)["norms"][0]}), flush=True)
         return
 
-    call = dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0)
+    theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+             if args.descent else None)
+    call = dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, params=theta,
+                       lr=DESCENT_LR, normalizer=DESCENT_L)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -373,7 +388,8 @@ def main():
         "dtype": datagen.configs.DTYPE_NAMES[w.dtype], "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "params": w.n_params,
                    "records_per_step": w.B, "tokens": w.T, "C": w.C, "sigma": w.sigma,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
         "roofline": roof, "cpu_baseline": cpu,
         "phases_ms": phase_ms, "gpu_ms_per_step": gpu_ms / args.steps,
         "wall_ms_per_step": wall * 1e3 / args.steps,

@@ -28,10 +28,12 @@ SUM_AUTO, SUM_GEMM, SUM_STORED = 0, 1, 2
 
 ACCUMULATE = 1
 NO_NOISE = 2
+DESCENT = 4
 
 EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
            "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_norms", "dpsgd_clip",
-           "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_step", "dpsgd_status", "dpsgd_layer_norm2",
+           "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_status",
+           "dpsgd_layer_norm2",
            "dpsgd_philox_raw", "dpsgd_error_string", "dpsgd_last_error")
 
 
@@ -57,7 +59,9 @@ class StepArgs(ctypes.Structure):
                 ("G", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.POINTER(ctypes.c_void_p)),
                 ("ws", ctypes.c_void_p), ("C", ctypes.c_double), ("sigma", ctypes.c_double),
                 ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64), ("flags", ctypes.c_uint32),
-                ("norms_out", ctypes.c_void_p), ("clip_out", ctypes.c_void_p)]
+                ("norms_out", ctypes.c_void_p), ("clip_out", ctypes.c_void_p),
+                ("params", ctypes.POINTER(ctypes.c_void_p)), ("lr", ctypes.c_double),
+                ("normalizer", ctypes.c_double)]
 
 
 _lib = None
@@ -85,6 +89,7 @@ def load():
         "dpsgd_clip": (ctypes.c_int, [P, I64, D, U32, P, P, P, P]),
         "dpsgd_clipped_sum": (ctypes.c_int, [P, I64, I32, I32, PP, PP, P, PP, U32, P, P]),
         "dpsgd_noise": (ctypes.c_int, [P, PP, D, D, U64, U64, P, P]),
+        "dpsgd_noise_descent": (ctypes.c_int, [P, PP, PP, D, D, U64, U64, D, D, P, P]),
         "dpsgd_step": (ctypes.c_int, [P, ctypes.POINTER(StepArgs), P]),
         "dpsgd_status": (ctypes.c_int, [P, P, P]),
         "dpsgd_layer_norm2": (ctypes.c_int, [P, I64, I32, I32, P, P, P]),
@@ -189,18 +194,30 @@ def clipped_sum(plan: Plan, n_records: int, l0: int, l1: int, A, G, clip_factors
                                     _stream(stream)))
 
 
-def noise(plan: Plan, out, C: float, sigma: float, seed: int, step: int, ws=None, stream=None):
-    _check(load().dpsgd_noise(plan.handle, _ptr_array(out), C, sigma, seed, step, _ptr(ws),
-                              _stream(stream)))
+def noise(plan: Plan, out, C: float, sigma: float, seed: int, step: int, ws=None, stream=None,
+          params=None, lr: float = 0.0, normalizer: float = 1.0):
+    """dpsgd_noise, or dpsgd_noise_descent when `params` (one fp32 buffer per layer) is given."""
+    if params is None:
+        _check(load().dpsgd_noise(plan.handle, _ptr_array(out), C, sigma, seed, step, _ptr(ws),
+                                  _stream(stream)))
+    else:
+        _check(load().dpsgd_noise_descent(plan.handle, _ptr_array(out), _ptr_array(params), C,
+                                          sigma, seed, step, lr, normalizer, _ptr(ws),
+                                          _stream(stream)))
 
 
 def step(plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int, step_idx: int,
          n_records: Optional[int] = None, flags: int = 0, norms_out=None, clip_out=None,
-         stream=None):
+         stream=None, params=None, lr: float = 0.0, normalizer: float = 1.0):
+    """dpsgd_step; with `params` (one fp32 buffer per layer) the descent step is added
+    (DESCENT flag set)."""
     n = plan.max_records if n_records is None else n_records
     a_arr, g_arr, o_arr = _ptr_array(A), _ptr_array(G), _ptr_array(out)
+    p_arr = _ptr_array(params)
+    if params is not None:
+        flags |= DESCENT
     args = StepArgs(n, a_arr, g_arr, o_arr, _ptr(ws), C, sigma, seed, step_idx, flags,
-                    _ptr(norms_out), _ptr(clip_out))
+                    _ptr(norms_out), _ptr(clip_out), p_arr, lr, normalizer)
     _check(load().dpsgd_step(plan.handle, ctypes.byref(args), _stream(stream)))
 
 
@@ -210,12 +227,16 @@ class StepCall:
 
     def __init__(self, plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int,
                  step_idx: int = 0, n_records: Optional[int] = None, flags: int = 0,
-                 norms_out=None, clip_out=None, stream=None):
+                 norms_out=None, clip_out=None, stream=None, params=None, lr: float = 0.0,
+                 normalizer: float = 1.0):
         self.plan = plan
-        self._keep = (_ptr_array(A), _ptr_array(G), _ptr_array(out))
+        self._keep = (_ptr_array(A), _ptr_array(G), _ptr_array(out), _ptr_array(params))
         n = plan.max_records if n_records is None else n_records
+        if params is not None:
+            flags |= DESCENT
         self.args = StepArgs(n, self._keep[0], self._keep[1], self._keep[2], _ptr(ws), C, sigma,
-                             seed, step_idx, flags, _ptr(norms_out), _ptr(clip_out))
+                             seed, step_idx, flags, _ptr(norms_out), _ptr(clip_out),
+                             self._keep[3], lr, normalizer)
         self.stream = _stream(stream)
         self._fn = load().dpsgd_step
         self._ref = ctypes.byref(self.args)

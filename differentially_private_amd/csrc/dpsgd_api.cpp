@@ -428,8 +428,9 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
     return DPSGD_OK;
 }
 
-int do_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, uint64_t seed,
-             uint64_t step, const void* ws, hipStream_t s) {
+// params (or null): the descent step params_l -= descent * out_l after the noise
+int do_noise(const dpsgd_plan* p, float* const* out, float* const* params, double descent, double C,
+             double sigma, uint64_t seed, uint64_t step, const void* ws, hipStream_t s) {
     const int L = (int)p->layers.size();
     NoiseArgs a;
     for (int l0 = 0; l0 < L; l0 += kNoiseMaxLayers) {
@@ -439,9 +440,11 @@ int do_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, uin
         a.seed = seed;
         a.step = step;
         a.scale = (float)(sigma * C);
+        a.descent = (float)descent;
         a.status = ws ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + p->status_off) : nullptr;
         for (int l = l0; l < l1; ++l) {
             a.out[l - l0] = out[l];
+            a.params[l - l0] = params ? params[l] : nullptr;
             a.off[l - l0] = p->layers[l].param_off;
         }
         a.off[l1 - l0] = p->layers[l1 - 1].param_off + p->layers[l1 - 1].n_params;
@@ -456,7 +459,7 @@ int do_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, uin
 // weighted sum and, unless NO_NOISE, the noise in one pass per layer group.
 int do_finalize(const dpsgd_plan* p, int64_t n_rec, double C, double sigma, uint64_t seed,
                 uint64_t step, uint32_t flags, void* ws, float* const* out, float* n_user,
-                float* c_user, hipStream_t s) {
+                float* c_user, float* const* params, double descent, hipStream_t s) {
     const bool inside = n_rec <= kFinalMaxRecords && n_rec * p->parts_total <= kFinalMaxClipWork;
     if (!inside)
         if (int rc = do_clip(p, n_rec, C, flags, ws, n_user, c_user, s)) return rc;
@@ -482,8 +485,10 @@ int do_finalize(const dpsgd_plan* p, int64_t n_rec, double C, double sigma, uint
         a.c_user = c_user;
         a.status = ws_status(ws, p);
         a.clip = ws_f(ws, p->c_off);
+        a.descent = (float)descent;
         for (int l = l0; l < l1; ++l) {
             a.out[l - l0] = out[l];
+            a.params[l - l0] = params ? params[l] : nullptr;
             a.src[l - l0] = ws_f(ws, p->layers[l].stored_off);
             a.off[l - l0] = p->layers[l].param_off;
         }
@@ -693,7 +698,38 @@ int dpsgd_noise(const dpsgd_plan* p, float* const* out, double C, double sigma, 
     if (!out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
     for (size_t l = 0; l < p->layers.size(); ++l)
         if (!out[l]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
-    return do_noise(p, out, C, sigma, seed, step, ws, (hipStream_t)stream);
+    return do_noise(p, out, nullptr, 0.0, C, sigma, seed, step, ws, (hipStream_t)stream);
+}
+
+namespace {
+
+// the descent step's arguments: one parameter buffer per layer, finite learning rate, finite
+// normaliser > 0
+int check_descent(const dpsgd_plan* p, float* const* params, double lr, double normalizer) {
+    if (!params) return fail(DPSGD_ERR_INVALID_ARG, "params array is NULL");
+    for (size_t l = 0; l < p->layers.size(); ++l)
+        if (!params[l]) return fail(DPSGD_ERR_INVALID_ARG, "null params pointer");
+    if (!std::isfinite(lr)) return fail(DPSGD_ERR_INVALID_ARG, "learning rate is not finite");
+    if (!(normalizer > 0.0) || !std::isfinite(normalizer))
+        return fail(DPSGD_ERR_INVALID_ARG, "normalizer must be finite and > 0");
+    if (!std::isfinite((float)(lr / normalizer)))
+        return fail(DPSGD_ERR_INVALID_ARG, "lr / normalizer overflows float32");
+    return DPSGD_OK;
+}
+
+}  // namespace
+
+int dpsgd_noise_descent(const dpsgd_plan* p, float* const* out, float* const* params, double C,
+                        double sigma, uint64_t seed, uint64_t step, double lr, double normalizer,
+                        const void* ws, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (int rc = check_c_sigma(C, sigma, true)) return rc;
+    if (ws && reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(DPSGD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (!out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
+    for (size_t l = 0; l < p->layers.size(); ++l)
+        if (!out[l]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
+    if (int rc = check_descent(p, params, lr, normalizer)) return rc;
+    return do_noise(p, out, params, lr / normalizer, C, sigma, seed, step, ws, (hipStream_t)stream);
 }
 
 int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
@@ -702,7 +738,14 @@ int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
     if (int rc = check_records(p, a->n_records)) return rc;
     if (int rc = check_c_sigma(a->C, a->sigma, true)) return rc;
     if (int rc = check_ws(a->ws)) return rc;
-    if (a->flags & ~(DPSGD_ACCUMULATE | DPSGD_NO_NOISE)) return fail(DPSGD_ERR_INVALID_ARG, "unknown flags");
+    if (a->flags & ~(DPSGD_ACCUMULATE | DPSGD_NO_NOISE | DPSGD_DESCENT)) return fail(DPSGD_ERR_INVALID_ARG, "unknown flags");
+    const bool descend = (a->flags & DPSGD_DESCENT) != 0;
+    if (descend && (a->flags & DPSGD_NO_NOISE))
+        return fail(DPSGD_ERR_INVALID_ARG, "DPSGD_DESCENT releases the sum: it needs the noise phase");
+    if (descend)
+        if (int rc = check_descent(p, a->params, a->lr, a->normalizer)) return rc;
+    float* const* params = descend ? a->params : nullptr;
+    const double descent = descend ? a->lr / a->normalizer : 0.0;
     const int L = (int)p->layers.size();
     if (!a->out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
     if (a->n_records > 0 && (!a->A || !a->G)) return fail(DPSGD_ERR_INVALID_ARG, "A or G array is NULL");
@@ -714,11 +757,11 @@ int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
     if (int rc = do_norms(p, a->n_records, 0, L, a->A, a->G, a->ws, s)) return rc;
     if (a->n_records > 0 && all_stored(p))
         return do_finalize(p, a->n_records, a->C, a->sigma, a->seed, a->step, a->flags, a->ws,
-                           a->out, a->norms_out, a->clip_out, s);
+                           a->out, a->norms_out, a->clip_out, params, descent, s);
     if (int rc = do_clip(p, a->n_records, a->C, a->flags, a->ws, a->norms_out, a->clip_out, s)) return rc;
     if (int rc = do_sum(p, a->n_records, 0, L, a->A, a->G, nullptr, a->out, a->flags, a->ws, s)) return rc;
     if (!(a->flags & DPSGD_NO_NOISE))
-        if (int rc = do_noise(p, a->out, a->C, a->sigma, a->seed, a->step, a->ws, s)) return rc;
+        if (int rc = do_noise(p, a->out, params, descent, a->C, a->sigma, a->seed, a->step, a->ws, s)) return rc;
     return DPSGD_OK;
 }
 

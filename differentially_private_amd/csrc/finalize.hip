@@ -3,7 +3,8 @@
 // flat parameter index e,
 //   out[e] (+)= sum_i c_i P_i[e] + sigma * C * Z[e]
 // ("Privacy-Preserving Machine Learning", DP-SGD phases 3-4: clip each record,
-// sum, add N(0, sigma^2 C^2 I) once).  When the partials are few, every block
+// sum, add N(0, sigma^2 C^2 I) once), optionally followed by the descent step
+// params[e] -= lr / L * out[e] (phase 5).  When the partials are few, every block
 // first recomputes all clip factors itself with exactly the arithmetic of the
 // clip_factor kernel (one wavefront per record, lanes striding the record's
 // partials in a fixed order, fp64 butterfly), so the factors are bitwise the
@@ -30,8 +31,10 @@ __global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
     const int64_t n_l = a.off[l + 1] - off;
     const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + tid) * 4;
     const bool active = x0 < n_l;
+    float* th = a.params[l];   // descent step target, or null
     const bool vec = active && x0 + 4 <= n_l && (n_l & 3) == 0 && (off & 3) == 0 &&
-                     ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.src[l])) & 15u) == 0;
+                     ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.src[l]) |
+                       reinterpret_cast<uintptr_t>(th)) & 15u) == 0;
     const float* src = a.src[l] + x0;
 
     // 1) the first batch of this thread's gradient-block loads, independent of the factors
@@ -109,6 +112,13 @@ __global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
         s[2] += a.scale * z[2];
         s[3] += a.scale * z[3];
         *o = s;
+        if (th) {
+            f32x4* tp = reinterpret_cast<f32x4*>(th + x0);
+            f32x4 t = *tp;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t[q] = fmaf(-a.descent, s[q], t[q]);
+            *tp = t;
+        }
         return;
     }
     for (int q = 0; q < 4; ++q) {
@@ -125,7 +135,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
         for (int64_t i = 0; i < a.n_rec; ++i) s += cf[i] * a.src[l][i * n_l + x];
         float* o = a.out[l] + x;
         if (a.accumulate) s = *o + s;
-        *o = s + a.scale * z;
+        const float v = s + a.scale * z;
+        *o = v;
+        if (th) th[x] = fmaf(-a.descent, v, th[x]);
     }
 }
 

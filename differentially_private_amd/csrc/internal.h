@@ -104,7 +104,9 @@ struct NoiseArgs {
     int32_t pad;
     uint64_t seed, step;
     float scale;                       // sigma * C
+    float descent;                     // lr / normalizer (with params)
     const uint32_t* status;
+    float* params[kNoiseMaxLayers];    // descent step targets, or all null
 };
 
 constexpr int kFinalMaxLayers = 48;
@@ -137,6 +139,9 @@ struct FinalizeArgs {
     uint32_t* status;
     // ... or read (second variant)
     const float* clip;
+    // descent step after the noise: params[l] -= descent * out[l] (null: none)
+    float* params[kFinalMaxLayers];
+    float descent;
 };
 
 constexpr int kDenseMaxLayers = 32;

@@ -26,8 +26,9 @@ __global__ __launch_bounds__(256) void k_noise(NoiseArgs a) {
     const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (x0 >= n_l) return;
     float* o = a.out[l] + x0;
+    float* th = a.params[l] ? a.params[l] + x0 : nullptr;   // descent step target
     if (x0 + 4 <= n_l && (off & 3) == 0 && (n_l & 3) == 0 &&
-        (reinterpret_cast<uintptr_t>(a.out[l]) & 15u) == 0) {
+        ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.params[l])) & 15u) == 0) {
         float z[4];
         gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
         f32x4 v = *reinterpret_cast<f32x4*>(o);
@@ -36,13 +37,21 @@ __global__ __launch_bounds__(256) void k_noise(NoiseArgs a) {
         v[2] += a.scale * z[2];
         v[3] += a.scale * z[3];
         *reinterpret_cast<f32x4*>(o) = v;
+        if (th) {
+            f32x4 t = *reinterpret_cast<f32x4*>(th);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t[q] = fmaf(-a.descent, v[q], t[q]);
+            *reinterpret_cast<f32x4*>(th) = t;
+        }
         return;
     }
     for (int q = 0; q < 4 && x0 + q < n_l; ++q) {
         const uint64_t e = (uint64_t)(off + x0 + q);
         float z4[4];
         gauss4(e >> 2, a.step, a.seed, z4);
-        o[q] += a.scale * z4[e & 3];
+        const float v = o[q] + a.scale * z4[e & 3];
+        o[q] = v;
+        if (th) th[q] = fmaf(-a.descent, v, th[q]);
     }
 }
 

@@ -77,6 +77,7 @@ extern "C" {
 /* ---- flags ---- */
 #define DPSGD_ACCUMULATE 1u /* add into out (and OR into the status) instead of overwriting */
 #define DPSGD_NO_NOISE 2u   /* dpsgd_step: skip the noise phase */
+#define DPSGD_DESCENT 4u    /* dpsgd_step: after the noise, the descent step on args->params */
 
 typedef struct dpsgd_layer_shape {
     int64_t d_in;
@@ -105,9 +106,13 @@ typedef struct dpsgd_step_args {
     double sigma;          /* noise multiplier, finite and >= 0 */
     uint64_t seed;         /* Philox key */
     uint64_t step;         /* Philox counter words 2-3 (e.g. the logical step index) */
-    uint32_t flags;        /* DPSGD_ACCUMULATE | DPSGD_NO_NOISE */
+    uint32_t flags;        /* DPSGD_ACCUMULATE | DPSGD_NO_NOISE | DPSGD_DESCENT */
     float* norms_out;      /* optional device [n_records]: n_i */
     float* clip_out;       /* optional device [n_records]: c_i */
+    /* DPSGD_DESCENT only (ignored otherwise): */
+    float* const* params;  /* n_layers device pointers, theta_l [d_in, d_out] float32, updated in place */
+    double lr;             /* learning rate eta, finite */
+    double normalizer;     /* the fixed public normaliser L, finite and > 0 */
 } dpsgd_step_args;
 
 /* Build a plan: validate shapes, choose the path of every layer and lay out
@@ -168,10 +173,25 @@ int dpsgd_clipped_sum(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int
 int dpsgd_noise(const dpsgd_plan* plan, float* const* out, double C, double sigma, uint64_t seed,
                 uint64_t step, const void* ws, void* stream);
 
+/* Phases 4-5 ("Privacy-Preserving Machine Learning", DP-SGD phases 4 and 5:
+ * the noise, then the descent step theta <- theta - eta * g~ / L with L the
+ * fixed public normaliser), in one pass over the flat parameter index:
+ * out_l[e] += sigma * C * Z[off_l + e] as dpsgd_noise does, then
+ * params_l[e] -= (lr / normalizer) * out_l[e] (fp32, lr / normalizer rounded
+ * to fp32).  out keeps the noised sum.  params: one device pointer per layer,
+ * [d_in, d_out] float32, overlapping no out buffer.  For virtual batching after
+ * the last physical batch.  Skipped on device (out and params untouched) while
+ * the status is NONFINITE (ws given). */
+int dpsgd_noise_descent(const dpsgd_plan* plan, float* const* out, float* const* params, double C,
+                        double sigma, uint64_t seed, uint64_t step, double lr, double normalizer,
+                        const void* ws, void* stream);
+
 /* The whole step: dpsgd_norms(all layers) -> dpsgd_clip -> dpsgd_clipped_sum
- * (all layers) -> dpsgd_noise unless DPSGD_NO_NOISE.  Virtual batching: call
+ * (all layers) -> dpsgd_noise unless DPSGD_NO_NOISE (dpsgd_noise_descent with
+ * DPSGD_DESCENT).  DPSGD_DESCENT with DPSGD_NO_NOISE is an INVALID_ARG: the
+ * update releases the sum, which must carry the noise.  Virtual batching: call
  * with DPSGD_NO_NOISE for every physical batch, DPSGD_ACCUMULATE for all but
- * the first, then dpsgd_noise once. */
+ * the first, then dpsgd_noise (or dpsgd_noise_descent) once. */
 int dpsgd_step(const dpsgd_plan* plan, const dpsgd_step_args* args, void* stream);
 
 /* Synchronise `stream` and read the status word: DPSGD_OK or

@@ -112,10 +112,11 @@ def plan():
 
 def _step(plan, **kw):
     a = dict(A=[P, P], G=[P, P], out=[P, P], ws=W, C=1.0, sigma=1.0, seed=0, step_idx=0,
-             n_records=4, flags=0, stream=0)
+             n_records=4, flags=0, stream=0, params=None, lr=0.01, normalizer=16.0)
     a.update(kw)
     return dp.step(plan, a["A"], a["G"], a["out"], a["ws"], a["C"], a["sigma"], a["seed"],
-                   a["step_idx"], n_records=a["n_records"], flags=a["flags"], stream=a["stream"])
+                   a["step_idx"], n_records=a["n_records"], flags=a["flags"], stream=a["stream"],
+                   params=a["params"], lr=a["lr"], normalizer=a["normalizer"])
 
 
 @pytest.mark.parametrize("kw", [dict(C=0.0), dict(C=-1.0), dict(C=float("nan")), dict(C=float("inf")),
@@ -127,6 +128,29 @@ def test_step_rejects_before_launch(plan, kw):
     with pytest.raises(dp.DpsgdError) as e:
         _step(plan, **kw)
     assert e.value.code == dp.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(flags=dp.DESCENT), dict(params=[P, None]),
+                                dict(params=[P, P], lr=float("nan")), dict(params=[P, P], lr=float("inf")),
+                                dict(params=[P, P], normalizer=0.0), dict(params=[P, P], normalizer=-1.0),
+                                dict(params=[P, P], normalizer=float("inf")),
+                                dict(params=[P, P], lr=1e300, normalizer=1e-10),
+                                dict(params=[P, P], lr=1e38, normalizer=1e-3),
+                                dict(params=[P, P], flags=dp.NO_NOISE)])
+def test_descent_rejects_before_launch(plan, kw):
+    """The descent step needs one parameter buffer per layer, a finite learning rate, a finite
+    normaliser > 0 whose quotient fits fp32, and the noise (an update without it would release
+    the un-noised sum)."""
+    with pytest.raises(dp.DpsgdError) as e:
+        _step(plan, **kw)
+    assert e.value.code == dp.ERR_INVALID_ARG
+    for bad in (dict(params=[P, None]), dict(params=[P, P], normalizer=0.0),
+                dict(params=[P, P], lr=float("nan"))):
+        k = dict(params=[P, P], lr=0.01, normalizer=16.0)
+        k.update(bad)
+        with pytest.raises(dp.DpsgdError) as e:
+            dp.noise(plan, [P, P], 1.0, 1.0, 0, 0, ws=W, stream=0, **k)
+        assert e.value.code == dp.ERR_INVALID_ARG
 
 
 def test_phase_entry_points_reject_before_launch(plan):
