@@ -403,3 +403,37 @@ def test_descent_step_noise_rms_page(golden_dir):
     step_norm = np.linalg.norm(r["theta"][0])
     assert round(step_norm, 2) == g["adapter_step_rms_2dp"]
     assert abs(step_norm - lr * g["sigma_c"] * math.sqrt(d) / L) < 5 * lr / (L * math.sqrt(2))
+
+
+def _users_as_records(users, d_out=1):
+    """Users as records: each user's token rows (one token per scalar gradient here) concatenated
+    and zero-padded to the longest user; zero rows add nothing to A^T G."""
+    T = max(len(u) for u in users)
+    A = np.zeros((len(users), T, 1))
+    G = np.zeros((len(users), T, d_out))
+    for i, u in enumerate(users):
+        A[i, :len(u), 0] = 1.0
+        G[i, :len(u), 0] = u
+    return [A], [G]
+
+
+def test_user_level_clipping_page(golden_dir):
+    """The page's sum-then-user-clip example: Alice's tickets 0.5 and 5.0 and Bao's 0.25 as two
+    users (each user's gradient is the sum over its records' token rows), C = 1: user-clipped
+    1.00 and 0.25; with the public normaliser 2 the sums are 0.625 with Alice and 0.125 without,
+    a change of 0.500 = C / 2 (example-level clipping gives Alice 1.50)."""
+    g = json.load(open(os.path.join(golden_dir, "p1_clip_example.json")))["alice_bao"]
+    u = g["user_level"]
+    A, G = _users_as_records([g["alice"], g["bao"]])
+    r = oracle.step(A, G, g["C"], 0.0, 0, 0)
+    assert np.allclose(r["n"] * r["c"], [u["alice_user_clipped"], u["bao_user_clipped"]], atol=1e-15)
+    with_alice = r["S"][0][0, 0] / u["normalizer"]
+    A1, G1 = _users_as_records([g["bao"]])
+    without_alice = oracle.step(A1, G1, g["C"], 0.0, 0, 0)["S"][0][0, 0] / u["normalizer"]
+    assert round(with_alice, 3) == u["with_alice"]
+    assert round(without_alice, 3) == u["without_alice"]
+    assert round(with_alice - without_alice, 3) == u["change"]
+    assert abs(with_alice - without_alice) <= g["C"] / u["normalizer"] + 1e-15
+    # example-level clipping of the same tickets gives Alice 1.50
+    Ar, Gr = _users_as_records([[v] for v in g["alice"]])
+    assert round(oracle.step(Ar, Gr, g["C"], 0.0, 0, 0)["S"][0][0, 0], 2) == g["alice_row_clipped_sum"]
