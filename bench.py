@@ -122,6 +122,59 @@ def sum_roofline(work, w, phase):
     return {"hbm_GBps": sb * w.n_phys / t / 1e9, "hbm_frac": sb * w.n_phys / t / 1e9 / HBM_PEAK_GBS}
 
 
+def users_line(args, w, torch, dev, dp, datagen):
+    """User-level clipping on workload 2's layers: 16 users, user u holding 1 + (u mod 4) of the
+    generator's 128-token records, each user's rows concatenated (40 records, 5,120 token rows,
+    at most 512 per user); one step clips each user's summed gradient."""
+    import numpy as np
+    recs = [1 + (u % 4) for u in range(16)]
+    lens = [r * w.T for r in recs]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n_users, T_max, n_rec = len(lens), max(lens), sum(recs)
+    plan = dp.Plan(w.layers, w.dtype, n_users, T_max, segments=True)
+    ws = plan.workspace(dev)
+    dp.ws_segments(plan, ws, offs)
+    As, Gs = device_inputs(w, datagen, torch, dev, 0, n_rec)          # records 0..39, contiguous
+    As = [a.reshape(-1, a.shape[2]) for a in As]
+    Gs = [g.reshape(-1, g.shape[2]) for g in Gs]
+    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    call = dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    assert dp.status(plan, ws) == dp.OK
+    a, b = ev(), ev()
+    a.record(stream)
+    for _ in range(args.steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    x0, x1 = ev(), ev()
+    x0.record(stream)
+    for _ in range(args.steps):
+        dp.norms(plan, n_users, 0, w.n_layers, As, Gs, ws)
+    x1.record(stream)
+    torch.cuda.synchronize()
+    norm_ms = x0.elapsed_time(x1) / args.steps
+    rows = int(offs[-1])
+    norm_bytes = rows * sum(di + do for di, do in w.layers) * 4 + n_users * w.n_params * 4
+    line = {"metric": "users/sec per DP-SGD step with user-level clipping", "value": n_users / (ms * 1e-3),
+            "unit": "users/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": datagen.configs.DTYPE_NAMES[w.dtype], "data": "synthetic",
+            "config": {"workload": w.name + "_users", "users": n_users, "records": n_rec,
+                       "token_rows": rows, "max_rows_per_user": T_max, "layers": w.n_layers,
+                       "params": w.n_params, "parallelism": "single GPU"},
+            "phases_ms": {"norms": norm_ms, "rest_of_step": ms - norm_ms},
+            "norms_roofline": {"hbm_GBps": norm_bytes / (norm_ms * 1e-3) / 1e9,
+                               "hbm_frac": norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "algorithmic_bytes": norm_bytes}}
+    print(json.dumps(line), flush=True)
+
+
 def secondary(args, w, torch, dev, dp, datagen):
     """Secondary lines for workloads 1, 3, 4, 5: one step = all physical batches of a logical
     batch (virtual batching: norms/clip/sum per physical batch, noise once), inputs resident in
@@ -263,6 +316,9 @@ def main():
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB "
                          "(the reference for scaling HBM byte counters)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--users", action="store_true",
+                    help="workload 2's layers with user-level clipping: 16 users of 1-4 records each "
+                         "(variable-length records, rows concatenated per user)")
     ap.add_argument("--descent", action="store_true",
                     help="fuse the descent step theta -= lr * noised sum / L into the timed step, with "
                          "lr 0.01 and L 1 (the sensitivity paper's release audit settings)")
@@ -298,6 +354,8 @@ def main():
                           "ms": ms, "GBps": 8 * n / ms / 1e6}), flush=True)
         return
     w = datagen.workload(args.workload)
+    if args.mode == "step" and args.users:
+        return users_line(args, w, torch, dev, dp, datagen)
     if args.mode == "step" and args.workload != 2:
         return secondary(args, w, torch, dev, dp, datagen)
     plan = dp.Plan(w.layers, w.dtype, w.B, w.T)

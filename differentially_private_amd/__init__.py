@@ -30,8 +30,10 @@ ACCUMULATE = 1
 NO_NOISE = 2
 DESCENT = 4
 
+PLAN_SEGMENTS = 1
+
 EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
-           "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_norms", "dpsgd_clip",
+           "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_ws_segments", "dpsgd_norms", "dpsgd_clip",
            "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_status",
            "dpsgd_layer_norm2",
            "dpsgd_philox_raw", "dpsgd_error_string", "dpsgd_last_error")
@@ -51,7 +53,7 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("layers", ctypes.POINTER(LayerShape)),
                 ("dtype", ctypes.c_int32), ("max_records", ctypes.c_int64),
                 ("tokens", ctypes.c_int64), ("path_policy", ctypes.c_int32),
-                ("sum_policy", ctypes.c_int32)]
+                ("sum_policy", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class StepArgs(ctypes.Structure):
@@ -85,6 +87,7 @@ def load():
         "dpsgd_plan_layer_info": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "dpsgd_plan_num_params": (I64, [P]),
         "dpsgd_ws_init": (ctypes.c_int, [P, P, P]),
+        "dpsgd_ws_segments": (ctypes.c_int, [P, P, ctypes.POINTER(I64), I64, P]),
         "dpsgd_norms": (ctypes.c_int, [P, I64, I32, I32, PP, PP, P, P]),
         "dpsgd_clip": (ctypes.c_int, [P, I64, D, U32, P, P, P, P]),
         "dpsgd_clipped_sum": (ctypes.c_int, [P, I64, I32, I32, PP, PP, P, PP, U32, P, P]),
@@ -137,15 +140,17 @@ def _stream(stream) -> int:
 
 
 class Plan:
-    """Host plan of dpsgd_plan_create: layer shapes, dtype, record capacity, tokens per record."""
+    """Host plan of dpsgd_plan_create: layer shapes, dtype, record capacity, tokens per record
+    (with segments=True: records are variable-length segments of at most `tokens` rows whose
+    offsets are set per workspace by ws_segments)."""
 
     def __init__(self, layers: Sequence[tuple], dtype: int, max_records: int, tokens: int,
-                 path_policy: int = PATH_AUTO, sum_policy: int = SUM_AUTO):
+                 path_policy: int = PATH_AUTO, sum_policy: int = SUM_AUTO, segments: bool = False):
         lib = load()
         self._layers = (LayerShape * len(layers))(*[LayerShape(int(a), int(b)) for a, b in layers]) \
             if len(layers) else None
         desc = PlanDesc(len(layers), self._layers, dtype, max_records, tokens, path_policy,
-                        sum_policy)
+                        sum_policy, PLAN_SEGMENTS if segments else 0)
         h = ctypes.c_void_p()
         ws = ctypes.c_size_t()
         _check(lib.dpsgd_plan_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws)))
@@ -170,6 +175,12 @@ class Plan:
     def workspace(self, device="cuda"):
         import torch
         return torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+
+def ws_segments(plan: Plan, ws, offsets, stream=None):
+    """dpsgd_ws_segments: record r owns token rows [offsets[r], offsets[r + 1])."""
+    arr = (ctypes.c_int64 * len(offsets))(*[int(v) for v in offsets])
+    _check(load().dpsgd_ws_segments(plan.handle, _ptr(ws), arr, len(offsets) - 1, _stream(stream)))
 
 
 def ws_init(plan: Plan, ws, stream=None):

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(128) void k_sum_direct(DirectArgs args) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        direct_block<DT, MB>(L.X, L.Y, rec, args.T, L.dX, L.dY, n0, m0, L.vec_x != 0, g, c, acc);
+        int64_t row0, len;
+        record_rows(args.seg, rec, args.T, row0, len);
+        direct_block<DT, MB>(L.X, L.Y, row0, len, L.dX, L.dY, n0, m0, L.vec_x != 0, g, c, acc);
         const float cf = args.clip[rec];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)

@@ -109,6 +109,19 @@ __device__ __forceinline__ void wait_copies(int64_t later) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// First token row and token count of record `rec`: fixed-length records (seg null) own rows
+// [rec T, rec T + T); variable-length records own rows [seg[rec], seg[rec + 1]).
+__device__ __forceinline__ void record_rows(const int64_t* seg, int64_t rec, int64_t T,
+                                            int64_t& row0, int64_t& len) {
+    if (seg) {
+        row0 = seg[rec];
+        len = seg[rec + 1] - row0;
+    } else {
+        row0 = rec * T;
+        len = T;
+    }
+}
+
 // v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of the A block and
 // column (l % 16) of the B block, each with 8 consecutive k of group l / 16;
 // the 16x16 fp32 result has column l % 16, rows 4 * (l / 16) + {0..3} in lane l.

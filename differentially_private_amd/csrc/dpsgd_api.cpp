@@ -81,7 +81,8 @@ struct dpsgd_plan {
     int64_t n_params;
     int n_splits_max;        // tile-engine GEMM sums
     int n_splits_dense_max;  // dense GEMM sums
-    int64_t status_off, parts_off, n_off, c_off;
+    bool segments;           // variable-length records (DPSGD_PLAN_SEGMENTS)
+    int64_t status_off, parts_off, n_off, c_off, seg_off;
     int64_t ws_bytes;
 };
 
@@ -94,6 +95,11 @@ bool ptr_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u
 float* ws_f(void* ws, int64_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
 uint32_t* ws_status(void* ws, const dpsgd_plan* p) {
     return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p->status_off);
+}
+// the segment table of a segment plan's workspace (null for fixed-length records)
+const int64_t* ws_seg(const void* ws, const dpsgd_plan* p) {
+    return p->segments ? reinterpret_cast<const int64_t*>(static_cast<const char*>(ws) + p->seg_off)
+                       : nullptr;
 }
 
 int check_plan(const dpsgd_plan* p) {
@@ -154,6 +160,7 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
             a.n_rec = n_rec;
             a.parts_stride = p->parts_total;
             a.parts = parts;
+            a.seg = ws_seg(ws, p);
             for (int l = l0; l < l1; ++l) {
                 const LayerPlan& lp = p->layers[l];
                 if (lp.path != DPSGD_PATH_DIRECT || lp.tiles.mb != mb ||
@@ -193,6 +200,7 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
     GramArgs g;
     std::memset(&g, 0, sizeof(g));
     g.T = p->T;
+    g.seg = ws_seg(ws, p);
     g.n_rec = n_rec;
     g.parts_stride = p->parts_total;
     g.parts = parts;
@@ -365,6 +373,7 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
         DirectArgs a;
         std::memset(&a, 0, sizeof(a));
         a.T = p->T;
+        a.seg = ws_seg(ws, p);
         a.n_rec = n_rec;
         a.clip = clip;
         a.rec_per_split = rps;
@@ -522,6 +531,7 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     if (d->max_records < 1 || d->max_records > 65535)
         return fail(DPSGD_ERR_INVALID_ARG, "max_records must be in [1, 65535]");
     if (d->tokens < 1) return fail(DPSGD_ERR_INVALID_ARG, "tokens (T) must be >= 1");
+    if (d->flags & ~DPSGD_PLAN_SEGMENTS) return fail(DPSGD_ERR_INVALID_ARG, "unknown plan flags");
     const int es = elem_size(d->dtype);
 
     dpsgd_plan* p = new (std::nothrow) dpsgd_plan();
@@ -529,6 +539,7 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     p->dtype = d->dtype;
     p->B = d->max_records;
     p->T = d->tokens;
+    p->segments = (d->flags & DPSGD_PLAN_SEGMENTS) != 0;
     int64_t param_off = 0, part_off = 0;
     for (int l = 0; l < d->n_layers; ++l) {
         const int64_t di = d->layers[l].d_in, dd = d->layers[l].d_out;
@@ -589,7 +600,8 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     int64_t waves = 0, dense_wgs = 0;
     for (LayerPlan& lp : p->layers) {
         if (lp.sum_mode != DPSGD_SUM_GEMM) continue;
-        lp.dense = p->dtype == DPSGD_DTYPE_BF16 && lp.tiles.mb == 2;
+        // (segment plans keep every GEMM sum on the tile engine, which walks each record's rows)
+        lp.dense = p->dtype == DPSGD_DTYPE_BF16 && lp.tiles.mb == 2 && !p->segments;
         if (lp.dense)
             dense_wgs += ((lp.d_in + 255) / 256) * ((lp.d_out + 255) / 256);
         else
@@ -615,6 +627,8 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     off = align_up(off + p->B * 4);
     p->c_off = off;
     off = align_up(off + p->B * 4);
+    p->seg_off = off;
+    if (p->segments) off = align_up(off + (p->B + 1) * 8);
     for (LayerPlan& lp : p->layers) {
         if (lp.sum_mode == DPSGD_SUM_STORED) {
             lp.stored_off = off;
@@ -647,6 +661,26 @@ int dpsgd_ws_init(const dpsgd_plan* p, void* ws, void* stream) {
     if (int rc = check_ws(ws)) return rc;
     hipError_t e = launch_status_clear(ws_status(ws, p), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "status clear launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_ws_segments(const dpsgd_plan* p, void* ws, const int64_t* offsets, int64_t n_records,
+                      void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (!p->segments) return fail(DPSGD_ERR_INVALID_ARG, "the plan was not created with DPSGD_PLAN_SEGMENTS");
+    if (int rc = check_ws(ws)) return rc;
+    if (int rc = check_records(p, n_records)) return rc;
+    if (!offsets) return fail(DPSGD_ERR_INVALID_ARG, "offsets is NULL");
+    if (offsets[0] != 0) return fail(DPSGD_ERR_INVALID_ARG, "offsets[0] must be 0");
+    for (int64_t r = 0; r < n_records; ++r) {
+        const int64_t len = offsets[r + 1] - offsets[r];
+        if (offsets[r + 1] < offsets[r] || len < 0 || len > p->T)
+            return fail(DPSGD_ERR_INVALID_ARG, "segment lengths must be in [0, tokens] (non-decreasing offsets)");
+    }
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + p->seg_off, offsets,
+                                  (size_t)(n_records + 1) * sizeof(int64_t), hipMemcpyHostToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "segment offsets copy");
     return DPSGD_OK;
 }
 

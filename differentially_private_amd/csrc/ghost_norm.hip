@@ -39,7 +39,9 @@ __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_d
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    direct_block<DT, MB>(L.X, L.Y, rec, args.T, L.dX, L.dY, n0, m0, L.vec_x != 0, g, c, acc);
+    int64_t row0, len;
+    record_rows(args.seg, rec, args.T, row0, len);
+    direct_block<DT, MB>(L.X, L.Y, row0, len, L.dX, L.dY, n0, m0, L.vec_x != 0, g, c, acc);
 
     float s = 0.f;
 #pragma unroll
@@ -60,11 +62,11 @@ __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_d
 // ---- Gram path ----
 
 template <int DT>
-__device__ __forceinline__ void gram_block(const void* M_, int64_t rec, int64_t T, int d, int t0,
+__device__ __forceinline__ void gram_block(const void* M_, int64_t row0, int64_t T, int d, int t0,
                                            int s0, bool vec, int g, int c, f32x4 (&acc)[4][4]) {
     const bool diag = (t0 == s0);
     if (DT == kBF16) {
-        const uint16_t* M = static_cast<const uint16_t*>(M_) + rec * T * d;
+        const uint16_t* M = static_cast<const uint16_t*>(M_) + row0 * d;
         for (int k0 = 0; k0 < d; k0 += 32) {
             const int k = k0 + 8 * g;
             const bool full = vec && (k + 8 <= d);
@@ -99,7 +101,7 @@ __device__ __forceinline__ void gram_block(const void* M_, int64_t rec, int64_t 
                 for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(av[mi], bv[ni], acc[mi][ni]);
         }
     } else {
-        const float* M = static_cast<const float*>(M_) + rec * T * d;
+        const float* M = static_cast<const float*>(M_) + row0 * d;
         for (int k0 = 0; k0 < d; k0 += 16) {
             const int k = k0 + 4 * g;
             const bool full = vec && (k + 4 <= d);
@@ -157,8 +159,10 @@ __global__ __launch_bounds__(256) void k_norm_gram(GramArgs args) {
             ga[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
             gg[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    gram_block<DT>(L.A, rec, args.T, L.d_in, t0, s0, L.vec_a != 0, g, c, ga);
-    gram_block<DT>(L.G, rec, args.T, L.d_out, t0, s0, L.vec_g != 0, g, c, gg);
+    int64_t row0, len;
+    record_rows(args.seg, rec, args.T, row0, len);
+    gram_block<DT>(L.A, row0, len, L.d_in, t0, s0, L.vec_a != 0, g, c, ga);
+    gram_block<DT>(L.G, row0, len, L.d_out, t0, s0, L.vec_g != 0, g, c, gg);
 
     float s = 0.f;
 #pragma unroll
@@ -336,7 +340,7 @@ hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store
 hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s) {
     // the copy kernel: bf16, rows 16-byte aligned, whole k-steps of features, and byte offsets
     // within a record below 2^31
-    bool copy = dtype == kBF16 && a.n_rec > 0;
+    bool copy = dtype == kBF16 && a.n_rec > 0 && !a.seg;
     for (int l = 0; l < a.n_layers; ++l) {
         const GramLayer& d = a.L[l];
         copy = copy && d.vec_a && d.vec_g && d.d_in % kGramK == 0 && d.d_out % kGramK == 0 &&

@@ -44,6 +44,7 @@ struct DirectArgs {
     const float* clip;         // SUM: per-record factors
     int64_t rec_per_split;     // SUM
     const uint32_t* status;    // SUM: skip while nonzero
+    const int64_t* seg;        // variable-length records: rows [seg[r], seg[r + 1]) (null: r T ..)
 };
 
 struct GramLayer {
@@ -65,6 +66,7 @@ struct GramArgs {
     int64_t n_rec;
     int64_t parts_stride;
     float* parts;
+    const int64_t* seg;        // variable-length records: rows [seg[r], seg[r + 1]) (null: r T ..)
 };
 
 struct ClipArgs {

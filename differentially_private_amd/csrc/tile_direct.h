@@ -158,17 +158,18 @@ __device__ __forceinline__ int direct_col(int n0, int c, int idx) {
     return n0 + 64 * (idx >> 2) + 4 * c + (idx & 3);
 }
 
+// The record's block over its T token rows starting at row0.
 template <int DT, int MB>
-__device__ __forceinline__ void direct_block(const void* X, const void* Y, int64_t rec, int64_t T,
+__device__ __forceinline__ void direct_block(const void* X, const void* Y, int64_t row0, int64_t T,
                                              int dX, int dY, int n0, int m0, bool vec_x, int g,
                                              int c, f32x4 (&acc)[MB][8]) {
     if (DT == kBF16) {
-        direct_block_bf16<MB>(static_cast<const uint16_t*>(X) + rec * T * dX,
-                              static_cast<const uint16_t*>(Y) + rec * T * dY, T, dX, dY, n0, m0,
+        direct_block_bf16<MB>(static_cast<const uint16_t*>(X) + row0 * dX,
+                              static_cast<const uint16_t*>(Y) + row0 * dY, T, dX, dY, n0, m0,
                               vec_x, g, c, acc);
     } else {
-        direct_block_f32<MB>(static_cast<const float*>(X) + rec * T * dX,
-                             static_cast<const float*>(Y) + rec * T * dY, T, dX, dY, n0, m0, vec_x,
+        direct_block_f32<MB>(static_cast<const float*>(X) + row0 * dX,
+                             static_cast<const float*>(Y) + row0 * dY, T, dX, dY, n0, m0, vec_x,
                              g, c, acc);
     }
 }

@@ -79,6 +79,15 @@ extern "C" {
 #define DPSGD_NO_NOISE 2u   /* dpsgd_step: skip the noise phase */
 #define DPSGD_DESCENT 4u    /* dpsgd_step: after the noise, the descent step on args->params */
 
+/* Plan flag: records are variable-length segments of token rows, e.g. users
+ * whose records' rows are concatenated ("Privacy-Preserving Machine Learning",
+ * user-level clipping: a user's vector is the sum of its records' gradients,
+ * A_u^T G_u over the concatenated rows, clipped as one).  Record r owns rows
+ * [off[r], off[r + 1]) of A_l [rows, d_in] and G_l [rows, d_out]; `tokens` is
+ * the longest segment; the offsets are set per workspace by dpsgd_ws_segments.
+ * Such plans run the register kernels (no dense copy kernels). */
+#define DPSGD_PLAN_SEGMENTS 1u
+
 typedef struct dpsgd_layer_shape {
     int64_t d_in;
     int64_t d_out;
@@ -92,14 +101,15 @@ typedef struct dpsgd_plan_desc {
     int64_t tokens;                  /* T, tokens per record (>= 1) */
     int32_t path_policy;             /* DPSGD_PATH_* */
     int32_t sum_policy;              /* DPSGD_SUM_* */
+    uint32_t flags;                  /* DPSGD_PLAN_SEGMENTS or 0 */
 } dpsgd_plan_desc;
 
 typedef struct dpsgd_plan dpsgd_plan; /* immutable host object */
 
 typedef struct dpsgd_step_args {
     int64_t n_records;     /* 0 <= n_records <= max_records (0: empty batch, noise only) */
-    const void* const* A;  /* n_layers device pointers, A_l [n_records, T, d_in] */
-    const void* const* G;  /* n_layers device pointers, G_l [n_records, T, d_out] */
+    const void* const* A;  /* n_layers device pointers, A_l [n_records, T, d_in] (segment plans: [rows, d_in]) */
+    const void* const* G;  /* n_layers device pointers, G_l [n_records, T, d_out] (segment plans: [rows, d_out]) */
     float* const* out;     /* n_layers device pointers, out_l [d_in, d_out] float32 */
     void* ws;              /* device workspace of dpsgd_plan_create's ws_bytes (256-B aligned) */
     double C;              /* clipping bound, finite and > 0 */
@@ -132,6 +142,15 @@ int dpsgd_plan_layer_info(const dpsgd_plan* plan, int32_t layer, int32_t* path, 
 
 /* Total trainable parameters sum_l d_in * d_out (the flat noise index space). */
 int64_t dpsgd_plan_num_params(const dpsgd_plan* plan);
+
+/* Segment plans only: set the token-row offsets of the next n_records records
+ * in `ws` (host array `offsets` of n_records + 1 entries: offsets[0] = 0,
+ * non-decreasing, each segment at most the plan's `tokens` rows; copied
+ * stream-ordered, the host array may be reused on return).  The following
+ * dpsgd_norms / dpsgd_clipped_sum / dpsgd_step calls on this workspace must
+ * use the same n_records.  Empty segments are allowed (norm 0, factor 1). */
+int dpsgd_ws_segments(const dpsgd_plan* plan, void* ws, const int64_t* offsets, int64_t n_records,
+                      void* stream);
 
 /* Clear the workspace status word (a fill kernel, no memset node).  Needed only
  * before a dpsgd_noise with a workspace that no dpsgd_clip has touched yet. */

@@ -180,3 +180,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dp, "_lib", None)
     with pytest.raises(RuntimeError):
         dp.load()
+
+
+def test_segment_offsets_rejected_before_copy():
+    """dpsgd_ws_segments checks the plan flag, the record count and every segment length
+    (offsets[0] = 0, non-decreasing, each at most `tokens` rows) before anything is copied."""
+    seg_plan = dp.Plan([(8, 8)], dp.DTYPE_F32, 3, 4, segments=True)
+    fixed = dp.Plan([(8, 8)], dp.DTYPE_F32, 3, 4)
+    for plan_, offs in ((fixed, [0, 2, 4]), (seg_plan, [1, 2, 4]), (seg_plan, [0, 3, 2]),
+                        (seg_plan, [0, 5]), (seg_plan, [0, 1, 2, 3, 4]), (seg_plan, [0, 4, 9])):
+        with pytest.raises(dp.DpsgdError) as e:
+            dp.ws_segments(plan_, W, offs, stream=0)
+        assert e.value.code == dp.ERR_INVALID_ARG, offs
+    with pytest.raises(dp.DpsgdError) as e:
+        dp.ws_segments(seg_plan, None, [0, 1], stream=0)
+    assert e.value.code == dp.ERR_INVALID_ARG
+
+
+def test_unknown_plan_flags_rejected():
+    lib = dp.load()
+    layers = (dp.LayerShape * 1)(dp.LayerShape(8, 8))
+    desc = dp.PlanDesc(1, layers, dp.DTYPE_F32, 4, 4, dp.PATH_AUTO, dp.SUM_AUTO, 2)
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.dpsgd_plan_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws)) == dp.ERR_INVALID_ARG
