@@ -122,6 +122,48 @@ def sum_roofline(work, w, phase):
     return {"hbm_GBps": sb * w.n_phys / t / 1e9, "hbm_frac": sb * w.n_phys / t / 1e9 / HBM_PEAK_GBS}
 
 
+def sample_line(args, torch, dev, dp):
+    """Poisson sampling of 2^27 records at q = 0.01 (the page's accountant example rate): K draws
+    (one per step index) between HIP events; the oracle's sampler on a 2^22-record sample for the
+    host rate; the library accountant's host time for the page's 300-step epsilon."""
+    import time
+    n, q = 1 << 27, 0.01
+    idx = torch.empty(n, dtype=torch.int64, device=dev)
+    cnt = torch.empty(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(dp.poisson_ws_bytes(n) // 8, dtype=torch.int64, device=dev)
+    mask = torch.empty(n, dtype=torch.uint8, device=dev)
+    for s in range(args.warmup):
+        dp.poisson_sample(1, s, q, n, idx, cnt, ws, mask=mask)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(args.steps):
+        dp.poisson_sample(1, s, q, n, idx, cnt, ws, mask=mask)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    sel = int(cnt.item())
+    from oracle import accountant as acc       # host baseline only
+    m = 1 << 22
+    t0 = time.perf_counter()
+    acc.poisson_sample(1, 0, q, m)
+    cpu_rate = m / (time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    per = dp.rdp_sampled_gaussian(q, 1.0, acc.DEFAULT_ORDERS)
+    eps, order = dp.rdp_to_epsilon(acc.DEFAULT_ORDERS, [300 * r for r in per], 1e-5)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    line = {"metric": "records/sec Poisson-sampled (inclusion mask + index list)", "value": n / (ms * 1e-3),
+            "unit": "records/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u32", "data": "synthetic",
+            "config": {"workload": "poisson_sampler", "population": n, "q": q, "selected_last": sel},
+            "bytes_written_GBps": (n + 8 * sel) / (ms * 1e-3) / 1e9,
+            "cpu_baseline": {"value": cpu_rate, "unit": "records/s", "cores": 1, "kind": "oracle",
+                             "sample": f"{m} records, one draw"},
+            "accountant": {"epsilon_300_steps": eps, "order": order, "host_ms": host_ms}}
+    print(json.dumps(line), flush=True)
+
+
 def users_line(args, w, torch, dev, dp, datagen):
     """User-level clipping on workload 2's layers: 16 users, user u holding 1 + (u mod 4) of the
     generator's 128-token records, each user's rows concatenated (40 records, 5,120 token rows,
@@ -311,7 +353,7 @@ def main():
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--manifest", default=None, help="write a run manifest JSON here")
-    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"],
+    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy", "sample"],
                     help="step: the benchmark; kernel: only the dominant kernel, --steps times "
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB "
                          "(the reference for scaling HBM byte counters)")
@@ -353,6 +395,8 @@ def main():
         print(json.dumps({"mode": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
                           "ms": ms, "GBps": 8 * n / ms / 1e6}), flush=True)
         return
+    if args.mode == "sample":
+        return sample_line(args, torch, dev, dp)
     w = datagen.workload(args.workload)
     if args.mode == "step" and args.users:
         return users_line(args, w, torch, dev, dp, datagen)

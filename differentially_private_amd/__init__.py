@@ -36,7 +36,9 @@ EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
            "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_ws_segments", "dpsgd_norms", "dpsgd_clip",
            "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_status",
            "dpsgd_layer_norm2",
-           "dpsgd_philox_raw", "dpsgd_error_string", "dpsgd_last_error")
+           "dpsgd_philox_raw", "dpsgd_poisson_ws_bytes", "dpsgd_poisson_sample",
+           "dpsgd_rdp_sampled_gaussian", "dpsgd_rdp_to_epsilon", "dpsgd_gaussian_pair_delta",
+           "dpsgd_gaussian_pair_epsilon", "dpsgd_error_string", "dpsgd_last_error")
 
 
 class DpsgdError(RuntimeError):
@@ -80,6 +82,7 @@ def load():
     P, I32, I64, U32, U64, D = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                 ctypes.c_uint64, ctypes.c_double)
     PP = ctypes.POINTER(ctypes.c_void_p)
+    PD = ctypes.POINTER(ctypes.c_double)
     sigs = {
         "dpsgd_plan_create": (ctypes.c_int, [ctypes.POINTER(PlanDesc), ctypes.POINTER(P),
                                              ctypes.POINTER(ctypes.c_size_t)]),
@@ -97,6 +100,12 @@ def load():
         "dpsgd_status": (ctypes.c_int, [P, P, P]),
         "dpsgd_layer_norm2": (ctypes.c_int, [P, I64, I32, I32, P, P, P]),
         "dpsgd_philox_raw": (ctypes.c_int, [U64, U64, U64, U64, P, P]),
+        "dpsgd_poisson_ws_bytes": (I64, [I64]),
+        "dpsgd_poisson_sample": (ctypes.c_int, [U64, U64, D, I64, P, P, P, P, P]),
+        "dpsgd_rdp_sampled_gaussian": (ctypes.c_int, [D, D, PD, I32, PD]),
+        "dpsgd_rdp_to_epsilon": (ctypes.c_int, [PD, PD, I32, D, I32, PD, PD]),
+        "dpsgd_gaussian_pair_delta": (ctypes.c_int, [D, D, PD]),
+        "dpsgd_gaussian_pair_epsilon": (ctypes.c_int, [D, D, PD]),
         "dpsgd_error_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dpsgd_last_error": (ctypes.c_char_p, []),
     }
@@ -275,3 +284,51 @@ def layer_norm2(plan: Plan, n_records: int, l0: int, l1: int, ws, out, stream=No
 
 def philox_raw(seed: int, step: int, first_block: int, n_blocks: int, out, stream=None):
     _check(load().dpsgd_philox_raw(seed, step, first_block, n_blocks, _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------- Poisson sampling
+
+def poisson_ws_bytes(population: int) -> int:
+    return load().dpsgd_poisson_ws_bytes(population)
+
+
+def poisson_sample(seed: int, step: int, q: float, population: int, indices, count, ws, mask=None,
+                   stream=None):
+    """dpsgd_poisson_sample: the included records' indices (increasing) into `indices`, their
+    number into `count` (device int64), the 0/1 inclusion bytes into `mask` if given."""
+    _check(load().dpsgd_poisson_sample(seed, step, q, population, _ptr(mask), _ptr(indices),
+                                       _ptr(count), _ptr(ws), _stream(stream)))
+
+
+# ---------------------------------------------------------------- privacy accounting (host)
+
+def _doubles(xs):
+    return (ctypes.c_double * len(xs))(*[float(x) for x in xs])
+
+
+def rdp_sampled_gaussian(q: float, sigma: float, orders) -> list:
+    """Per-step RDP of the Poisson-subsampled Gaussian mechanism at each order."""
+    o = _doubles(orders)
+    out = (ctypes.c_double * len(orders))()
+    _check(load().dpsgd_rdp_sampled_gaussian(q, sigma, o, len(orders), out))
+    return list(out)
+
+
+def rdp_to_epsilon(orders, rdp, delta: float, tight: bool = True):
+    """(epsilon, minimising order) at delta from RDP values at `orders`."""
+    e, a = ctypes.c_double(), ctypes.c_double()
+    _check(load().dpsgd_rdp_to_epsilon(_doubles(orders), _doubles(rdp), len(orders), delta,
+                                       1 if tight else 0, ctypes.byref(e), ctypes.byref(a)))
+    return e.value, a.value
+
+
+def gaussian_pair_delta(eps: float, mu: float) -> float:
+    d = ctypes.c_double()
+    _check(load().dpsgd_gaussian_pair_delta(eps, mu, ctypes.byref(d)))
+    return d.value
+
+
+def gaussian_pair_epsilon(delta: float, mu: float) -> float:
+    e = ctypes.c_double()
+    _check(load().dpsgd_gaussian_pair_epsilon(delta, mu, ctypes.byref(e)))
+    return e.value

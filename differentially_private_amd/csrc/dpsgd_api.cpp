@@ -847,6 +847,68 @@ int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_
     return DPSGD_OK;
 }
 
+int64_t dpsgd_poisson_ws_bytes(int64_t population) {
+    if (population < 0) return -1;
+    return std::max<int64_t>(16, 16 * sample_wgs(population));
+}
+
+int dpsgd_poisson_sample(uint64_t seed, uint64_t step, double q, int64_t population, uint8_t* mask,
+                         int64_t* indices, int64_t* count, void* ws, void* stream) {
+    if (!(q >= 0.0 && q <= 1.0)) return fail(DPSGD_ERR_INVALID_ARG, "q must be in [0, 1]");
+    if (population < 0 || population > ((int64_t)1 << 36))
+        return fail(DPSGD_ERR_INVALID_ARG, "population must be in [0, 2^36]");
+    if (!count) return fail(DPSGD_ERR_INVALID_ARG, "count is NULL");
+    if (population > 0 && (!indices || !ws)) return fail(DPSGD_ERR_INVALID_ARG, "indices or ws is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(DPSGD_ERR_INVALID_ARG, "ws is not 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(mask) % 4) return fail(DPSGD_ERR_INVALID_ARG, "mask is not 4-byte aligned");
+    const uint64_t thr = (uint64_t)std::floor(q * 4294967296.0);
+    hipError_t e = launch_poisson_sample(seed, step, thr, population, mask, indices, count,
+                                         static_cast<int64_t*>(ws), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "poisson sample launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_rdp_sampled_gaussian(double q, double sigma, const double* orders, int32_t n_orders,
+                               double* rdp_out) {
+    if (!(q >= 0.0 && q <= 1.0)) return fail(DPSGD_ERR_INVALID_ARG, "q must be in [0, 1]");
+    if (!(sigma > 0.0) || !std::isfinite(sigma)) return fail(DPSGD_ERR_INVALID_ARG, "sigma must be finite and > 0");
+    if (n_orders < 1 || !orders || !rdp_out) return fail(DPSGD_ERR_INVALID_ARG, "orders or rdp_out missing");
+    for (int k = 0; k < n_orders; ++k)
+        if (!(orders[k] > 1.0) || !std::isfinite(orders[k]))
+            return fail(DPSGD_ERR_INVALID_ARG, "orders must be finite and > 1");
+    for (int k = 0; k < n_orders; ++k) rdp_out[k] = rdp_sampled_gaussian(q, sigma, orders[k]);
+    return DPSGD_OK;
+}
+
+int dpsgd_rdp_to_epsilon(const double* orders, const double* rdp, int32_t n_orders, double delta,
+                         int32_t tight, double* eps_out, double* order_out) {
+    if (!(delta > 0.0 && delta < 1.0)) return fail(DPSGD_ERR_INVALID_ARG, "delta must be in (0, 1)");
+    if (n_orders < 1 || !orders || !rdp || !eps_out) return fail(DPSGD_ERR_INVALID_ARG, "orders, rdp or eps_out missing");
+    for (int k = 0; k < n_orders; ++k) {
+        if (!(orders[k] > 1.0) || !std::isfinite(orders[k]))
+            return fail(DPSGD_ERR_INVALID_ARG, "orders must be finite and > 1");
+        if (!(rdp[k] >= 0.0)) return fail(DPSGD_ERR_INVALID_ARG, "rdp values must be >= 0");
+    }
+    *eps_out = rdp_epsilon(orders, rdp, n_orders, delta, tight != 0, order_out);
+    return DPSGD_OK;
+}
+
+int dpsgd_gaussian_pair_delta(double eps, double mu, double* delta_out) {
+    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(DPSGD_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!(mu > 0.0) || !std::isfinite(mu)) return fail(DPSGD_ERR_INVALID_ARG, "mu must be finite and > 0");
+    if (!delta_out) return fail(DPSGD_ERR_INVALID_ARG, "delta_out is NULL");
+    *delta_out = gaussian_pair_delta(eps, mu);
+    return DPSGD_OK;
+}
+
+int dpsgd_gaussian_pair_epsilon(double delta, double mu, double* eps_out) {
+    if (!(delta > 0.0 && delta < 1.0)) return fail(DPSGD_ERR_INVALID_ARG, "delta must be in (0, 1)");
+    if (!(mu > 0.0) || !std::isfinite(mu)) return fail(DPSGD_ERR_INVALID_ARG, "mu must be finite and > 0");
+    if (!eps_out) return fail(DPSGD_ERR_INVALID_ARG, "eps_out is NULL");
+    *eps_out = gaussian_pair_epsilon(delta, mu);
+    return DPSGD_OK;
+}
+
 const char* dpsgd_error_string(int code) {
     switch (code) {
         case DPSGD_OK: return "ok";

@@ -196,4 +196,16 @@ hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s);
 hipError_t launch_sum_dense(const DenseSumArgs& a, int n_splits, hipStream_t s);
 
+// privacy accounting (host)
+double rdp_sampled_gaussian(double q, double sigma, double alpha);
+double rdp_epsilon(const double* orders, const double* rdp, int n, double delta, bool tight,
+                   double* best_order);
+double gaussian_pair_delta(double eps, double mu);
+double gaussian_pair_epsilon(double delta, double mu);
+
+// Poisson sampler: ws holds 2 * sample_wgs(n) int64
+int64_t sample_wgs(int64_t n);
+hipError_t launch_poisson_sample(uint64_t seed, uint64_t step, uint64_t thr, int64_t n, uint8_t* mask,
+                                 int64_t* indices, int64_t* count, int64_t* ws, hipStream_t s);
+
 }  // namespace dpsgd

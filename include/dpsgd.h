@@ -213,6 +213,41 @@ int dpsgd_noise_descent(const dpsgd_plan* plan, float* const* out, float* const*
  * the first, then dpsgd_noise (or dpsgd_noise_descent) once. */
 int dpsgd_step(const dpsgd_plan* plan, const dpsgd_step_args* args, void* stream);
 
+/* Poisson sampling of a step's records ("Privacy-Preserving Machine Learning",
+ * DP-SGD phase 1: each of `population` records included independently with
+ * public probability q, 0 <= q <= 1).  Record i draws word i mod 4 of
+ * Philox4x32-10 block 2^63 + floor(i / 4) (key = seed, counter words 2-3 =
+ * step; the top bit keeps these words apart from the noise stream) and is
+ * included iff that word < floor(q * 2^32).  Device outputs: `indices` (room
+ * for `population` int64; the included records in increasing order), `count`
+ * (one int64), optional `mask` (population bytes, 0/1, 4-byte aligned).  `ws`:
+ * device scratch of dpsgd_poisson_ws_bytes(population) bytes, 8-byte aligned
+ * (may be NULL when population is 0).  population <= 2^36. */
+int64_t dpsgd_poisson_ws_bytes(int64_t population);
+int dpsgd_poisson_sample(uint64_t seed, uint64_t step, double q, int64_t population, uint8_t* mask,
+                         int64_t* indices, int64_t* count, void* ws, void* stream);
+
+/* Privacy accounting, host only ("Privacy-Preserving Machine Learning",
+ * section on privacy accounting: RDP bounds add over steps and convert to
+ * (epsilon, delta)).  dpsgd_rdp_sampled_gaussian: per-step Renyi DP at each
+ * order (> 1) of the Poisson-subsampled Gaussian mechanism, sampling
+ * probability q in [0, 1], noise multiplier sigma > 0 (multiply by the number
+ * of steps to compose; alpha / (2 sigma^2) at q = 1).  dpsgd_rdp_to_epsilon:
+ * epsilon at delta in (0, 1), minimised over the orders, with the conservative
+ * conversion rdp + log(1/delta) / (alpha - 1) (tight = 0) or the tighter
+ * rdp + log((alpha - 1) / alpha) - (log delta + log alpha) / (alpha - 1)
+ * (tight = 1); order_out (optional) receives the minimising order.
+ * dpsgd_gaussian_pair_delta / _epsilon: Eq. 5 of "Sensitivity Inflation from
+ * Cross-Record Precision Routing in Private Quantized Fine-Tuning" (Sec. 3.2),
+ * delta(eps) = Phi(mu/2 - eps/mu) - e^eps Phi(-mu/2 - eps/mu) for a one-step
+ * Gaussian release with mu = Delta / (sigma C) > 0, and its inverse. */
+int dpsgd_rdp_sampled_gaussian(double q, double sigma, const double* orders, int32_t n_orders,
+                               double* rdp_out);
+int dpsgd_rdp_to_epsilon(const double* orders, const double* rdp, int32_t n_orders, double delta,
+                         int32_t tight, double* eps_out, double* order_out);
+int dpsgd_gaussian_pair_delta(double eps, double mu, double* delta_out);
+int dpsgd_gaussian_pair_epsilon(double delta, double mu, double* eps_out);
+
 /* Synchronise `stream` and read the status word: DPSGD_OK or
  * DPSGD_ERR_NONFINITE (or DPSGD_ERR_HIP). */
 int dpsgd_status(const dpsgd_plan* plan, const void* ws, void* stream);
