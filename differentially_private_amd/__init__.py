@@ -38,7 +38,9 @@ EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
            "dpsgd_layer_norm2",
            "dpsgd_philox_raw", "dpsgd_poisson_ws_bytes", "dpsgd_poisson_sample",
            "dpsgd_rdp_sampled_gaussian", "dpsgd_rdp_to_epsilon", "dpsgd_gaussian_pair_delta",
-           "dpsgd_gaussian_pair_epsilon", "dpsgd_error_string", "dpsgd_last_error")
+           "dpsgd_gaussian_pair_epsilon", "dpsgd_i8_pitch", "dpsgd_i8_plan_create",
+           "dpsgd_i8_plan_destroy", "dpsgd_i8_quantize_weight", "dpsgd_i8_set_records",
+           "dpsgd_i8_forward", "dpsgd_i8_route", "dpsgd_i8_matmul", "dpsgd_i8_intermediates", "dpsgd_error_string", "dpsgd_last_error")
 
 
 class DpsgdError(RuntimeError):
@@ -106,6 +108,16 @@ def load():
         "dpsgd_rdp_to_epsilon": (ctypes.c_int, [PD, PD, I32, D, I32, PD, PD]),
         "dpsgd_gaussian_pair_delta": (ctypes.c_int, [D, D, PD]),
         "dpsgd_gaussian_pair_epsilon": (ctypes.c_int, [D, D, PD]),
+        "dpsgd_i8_pitch": (I64, [I64]),
+        "dpsgd_i8_plan_create": (ctypes.c_int, [I64, I64, I64, ctypes.POINTER(P),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+        "dpsgd_i8_plan_destroy": (None, [P]),
+        "dpsgd_i8_quantize_weight": (ctypes.c_int, [P, I64, I64, P, P, P]),
+        "dpsgd_i8_set_records": (ctypes.c_int, [P, P, ctypes.POINTER(I64), I64, P]),
+        "dpsgd_i8_forward": (ctypes.c_int, [P, P, I64, I64, P, I64, P, P, I64, ctypes.c_float, P, P]),
+        "dpsgd_i8_route": (ctypes.c_int, [P, P, I64, I64, P, I64, ctypes.c_float, P]),
+        "dpsgd_i8_matmul": (ctypes.c_int, [P, P, I64, I64, P, I64, P, P, I64, P, P]),
+        "dpsgd_i8_intermediates": (ctypes.c_int, [P, P, I64, I64, I64, P, P, P, P, P]),
         "dpsgd_error_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dpsgd_last_error": (ctypes.c_char_p, []),
     }
@@ -332,3 +344,73 @@ def gaussian_pair_epsilon(delta: float, mu: float) -> float:
     e = ctypes.c_double()
     _check(load().dpsgd_gaussian_pair_epsilon(delta, mu, ctypes.byref(e)))
     return e.value
+
+
+# ---------------------------------------------------------------- record-owned INT8 forward
+
+def i8_pitch(k: int) -> int:
+    """Bytes per INT8 code row (k rounded up to 64; 0 for k outside [1, 32768])."""
+    return load().dpsgd_i8_pitch(k)
+
+
+class I8Plan:
+    """Host plan of dpsgd_i8_plan_create: capacities of the INT8 forward's workspace."""
+
+    def __init__(self, max_rows: int, max_records: int, max_k: int):
+        lib = load()
+        h = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        _check(lib.dpsgd_i8_plan_create(max_rows, max_records, max_k, ctypes.byref(h),
+                                        ctypes.byref(ws)))
+        self.handle = h
+        self.ws_bytes = ws.value
+        self.max_rows, self.max_records, self.max_k = max_rows, max_records, max_k
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.dpsgd_i8_plan_destroy(self.handle)
+            self.handle = None
+
+    def workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+
+def i8_quantize_weight(W, n_out: int, k: int, wq, w_scale, stream=None):
+    """dpsgd_i8_quantize_weight: W fp16 [n_out, k] -> wq int8 [n_out, pitch(k)], w_scale fp32."""
+    _check(load().dpsgd_i8_quantize_weight(_ptr(W), n_out, k, _ptr(wq), _ptr(w_scale),
+                                           _stream(stream)))
+
+
+def i8_set_records(plan: I8Plan, ws, offsets, stream=None):
+    """dpsgd_i8_set_records: record r owns activation rows [offsets[r], offsets[r + 1])."""
+    arr = (ctypes.c_int64 * len(offsets))(*[int(v) for v in offsets])
+    _check(load().dpsgd_i8_set_records(plan.handle, _ptr(ws), arr, len(offsets) - 1,
+                                       _stream(stream)))
+
+
+def i8_forward(plan: I8Plan, ws, n_rows: int, n_records: int, A, k: int, wq, w_scale, n_out: int,
+               tau: float, Y, stream=None):
+    """dpsgd_i8_forward: Y [n_rows, n_out] fp16 = record-owned LLM.int8 forward of A."""
+    _check(load().dpsgd_i8_forward(plan.handle, _ptr(ws), n_rows, n_records, _ptr(A), k,
+                                   _ptr(wq), _ptr(w_scale), n_out, tau, _ptr(Y), _stream(stream)))
+
+
+def i8_route(plan: I8Plan, ws, n_rows: int, n_records: int, A, k: int, tau: float, stream=None):
+    """dpsgd_i8_route: Algorithm 1's steps 1-6 into the workspace."""
+    _check(load().dpsgd_i8_route(plan.handle, _ptr(ws), n_rows, n_records, _ptr(A), k, tau,
+                                 _stream(stream)))
+
+
+def i8_matmul(plan: I8Plan, ws, n_rows: int, n_records: int, A, k: int, wq, w_scale, n_out: int, Y,
+              stream=None):
+    """dpsgd_i8_matmul: step 7 after a dpsgd_i8_route of the same activations."""
+    _check(load().dpsgd_i8_matmul(plan.handle, _ptr(ws), n_rows, n_records, _ptr(A), k, _ptr(wq),
+                                  _ptr(w_scale), n_out, _ptr(Y), _stream(stream)))
+
+
+def i8_intermediates(plan: I8Plan, ws, n_rows: int, n_records: int, k: int, q=None,
+                     row_scale=None, outlier_mask=None, owner=None, stream=None):
+    _check(load().dpsgd_i8_intermediates(plan.handle, _ptr(ws), n_rows, n_records, k, _ptr(q),
+                                         _ptr(row_scale), _ptr(outlier_mask), _ptr(owner),
+                                         _stream(stream)))

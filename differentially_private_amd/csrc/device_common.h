@@ -109,6 +109,24 @@ __device__ __forceinline__ void wait_copies(int64_t later) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Tile of this workgroup among tiles_m x tiles_n.  Workgroup ids go round-robin over the 8 XCDs
+// (ids x, x + 8, ... run on XCD x); those get consecutive logical ids, and logical ids walk groups
+// of group_m tile rows column by column, so the workgroups resident on one XCD cover a compact
+// block of tiles and share their A and G column bands through that XCD's L2.
+__device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    const int n_tiles = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if (t >= n_tiles) return false;
+    if (n_tiles % 8 == 0) t = (t % 8) * (n_tiles / 8) + t / 8;
+    const int group = t / (group_m * tiles_n);
+    const int first_m = group * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = t - group * group_m * tiles_n;
+    tm = first_m + r % gm;
+    tn = r / gm;
+    return true;
+}
+
 // First token row and token count of record `rec`: fixed-length records (seg null) own rows
 // [rec T, rec T + T); variable-length records own rows [seg[rec], seg[rec + 1]).
 __device__ __forceinline__ void record_rows(const int64_t* seg, int64_t rec, int64_t T,

@@ -516,6 +516,15 @@ bool all_stored(const dpsgd_plan* p) {
 
 }  // namespace
 
+// Host plan of the record-owned INT8 forward: capacities and the workspace layout.
+struct I8PlanImpl {
+    int64_t max_rows, max_records, max_k, kp, kw;
+    int64_t off_offsets, off_own, off_s, off_omask, off_q, ws_bytes;
+};
+
+int64_t i8_pitch(int64_t k) { return (k + 63) / 64 * 64; }
+
+
 extern "C" {
 
 int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_bytes) {
@@ -908,6 +917,194 @@ int dpsgd_gaussian_pair_epsilon(double delta, double mu, double* eps_out) {
     *eps_out = gaussian_pair_epsilon(delta, mu);
     return DPSGD_OK;
 }
+
+// ---------------------------------------------------------------- record-owned INT8 forward
+
+struct dpsgd_i8_plan : I8PlanImpl {};
+
+int64_t dpsgd_i8_pitch(int64_t k) { return k >= 1 && k <= kI8MaxKW * 32 ? i8_pitch(k) : 0; }
+
+int dpsgd_i8_plan_create(int64_t max_rows, int64_t max_records, int64_t max_k, dpsgd_i8_plan** out,
+                         size_t* ws_bytes) {
+    if (!out || !ws_bytes) return fail(DPSGD_ERR_INVALID_ARG, "out or ws_bytes is NULL");
+    *out = nullptr;
+    if (max_rows < 0 || max_records < 1 || max_k < 1 || max_k > kI8MaxKW * 32)
+        return fail(DPSGD_ERR_INVALID_ARG, "need max_rows >= 0, max_records >= 1, 1 <= max_k <= 32768");
+    const int64_t kp = i8_pitch(max_k), kw = (max_k + 31) / 32;
+    if (max_rows * kp >= ((int64_t)1 << 31))
+        return fail(DPSGD_ERR_INVALID_ARG, "max_rows * pitch(max_k) must be below 2^31 bytes");
+    if (max_records > ((int64_t)1 << 31) / kw)
+        return fail(DPSGD_ERR_INVALID_ARG, "max_records too large");
+    dpsgd_i8_plan* p = new (std::nothrow) dpsgd_i8_plan();
+    if (!p) return fail(DPSGD_ERR_INVALID_ARG, "out of host memory");
+    p->max_rows = max_rows;
+    p->max_records = max_records;
+    p->max_k = max_k;
+    p->kp = kp;
+    p->kw = kw;
+    int64_t off = 0;
+    p->off_offsets = off;
+    off = align_up(off + (max_records + 1) * 8);
+    p->off_own = off;
+    off = align_up(off + max_rows * 4);
+    p->off_s = off;
+    off = align_up(off + max_rows * 4);
+    p->off_omask = off;
+    off = align_up(off + max_records * kw * 4);
+    p->off_q = off;
+    off = align_up(off + max_rows * kp);
+    p->ws_bytes = off;
+    *out = p;
+    *ws_bytes = (size_t)off;
+    return DPSGD_OK;
+}
+
+void dpsgd_i8_plan_destroy(dpsgd_i8_plan* p) { delete p; }
+
+int dpsgd_i8_set_records(const dpsgd_i8_plan* p, void* ws, const int64_t* offsets, int64_t n_records,
+                         void* stream) {
+    if (!p) return fail(DPSGD_ERR_INVALID_ARG, "plan is NULL");
+    if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return fail(DPSGD_ERR_INVALID_ARG, "ws is NULL or not 256-byte aligned");
+    if (n_records < 1 || n_records > p->max_records) return fail(DPSGD_ERR_INVALID_ARG, "n_records must be in [1, max_records]");
+    if (!offsets) return fail(DPSGD_ERR_INVALID_ARG, "offsets is NULL");
+    if (offsets[0] != 0) return fail(DPSGD_ERR_INVALID_ARG, "offsets[0] must be 0");
+    for (int64_t r = 0; r < n_records; ++r)
+        if (offsets[r + 1] < offsets[r]) return fail(DPSGD_ERR_INVALID_ARG, "offsets must be non-decreasing");
+    if (offsets[n_records] > p->max_rows) return fail(DPSGD_ERR_INVALID_ARG, "offsets[n_records] exceeds max_rows");
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_offsets, offsets,
+                                  (size_t)(n_records + 1) * sizeof(int64_t), hipMemcpyHostToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "record offsets copy");
+    return DPSGD_OK;
+}
+
+int dpsgd_i8_quantize_weight(const uint16_t* w, int64_t n_out, int64_t k, int8_t* wq, float* w_scale,
+                             void* stream) {
+    if (k < 1 || k > kI8MaxKW * 32) return fail(DPSGD_ERR_INVALID_ARG, "k must be in [1, 32768]");
+    if (n_out < 0) return fail(DPSGD_ERR_INVALID_ARG, "n_out must be >= 0");
+    if (n_out > 0 && (!w || !wq || !w_scale)) return fail(DPSGD_ERR_INVALID_ARG, "null pointer");
+    hipError_t e = launch_i8_weight(w, n_out, k, i8_pitch(k), wq, w_scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "weight quantisation launch");
+    return DPSGD_OK;
+}
+
+namespace {
+
+int i8_args(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_records, int64_t k,
+            I8Args& a) {
+    if (!p) return fail(DPSGD_ERR_INVALID_ARG, "plan is NULL");
+    if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return fail(DPSGD_ERR_INVALID_ARG, "ws is NULL or not 256-byte aligned");
+    if (n_rows < 0 || n_rows > p->max_rows) return fail(DPSGD_ERR_INVALID_ARG, "n_rows must be in [0, max_rows]");
+    if (n_records < 1 || n_records > p->max_records) return fail(DPSGD_ERR_INVALID_ARG, "n_records must be in [1, max_records]");
+    if (k < 1 || k > p->max_k) return fail(DPSGD_ERR_INVALID_ARG, "k must be in [1, max_k]");
+    char* w = static_cast<char*>(ws);
+    a = I8Args{};
+    a.n = n_rows;
+    a.K = k;
+    a.Kp = i8_pitch(k);
+    a.KW = (k + 31) / 32;
+    a.n_rec = n_records;
+    a.offsets = reinterpret_cast<const int64_t*>(w + p->off_offsets);
+    a.own = reinterpret_cast<int32_t*>(w + p->off_own);
+    a.s = reinterpret_cast<float*>(w + p->off_s);
+    a.omask = reinterpret_cast<uint32_t*>(w + p->off_omask);
+    a.Q = reinterpret_cast<int8_t*>(w + p->off_q);
+    return DPSGD_OK;
+}
+
+}  // namespace
+
+namespace {
+
+int i8_check_a(const I8Args& a, const uint16_t* a_in, float tau) {
+    if (std::isnan(tau)) return fail(DPSGD_ERR_INVALID_ARG, "tau is NaN");
+    if (a.n > 0 && !a_in) return fail(DPSGD_ERR_INVALID_ARG, "a is NULL");
+    return DPSGD_OK;
+}
+
+int i8_check_w(I8Args& a, const int8_t* wq, const float* w_scale, int64_t n_out, uint16_t* y) {
+    if (n_out < 0) return fail(DPSGD_ERR_INVALID_ARG, "n_out must be >= 0");
+    if (n_out * a.Kp >= ((int64_t)1 << 31)) return fail(DPSGD_ERR_INVALID_ARG, "n_out * pitch(k) must be below 2^31 bytes");
+    if (n_out > 0 && (!wq || !w_scale)) return fail(DPSGD_ERR_INVALID_ARG, "wq or w_scale is NULL");
+    if (a.n > 0 && n_out > 0 && !y) return fail(DPSGD_ERR_INVALID_ARG, "y is NULL");
+    if (reinterpret_cast<uintptr_t>(wq) % 16) return fail(DPSGD_ERR_INVALID_ARG, "wq must be 16-byte aligned");
+    a.Wq = wq;
+    a.sW = w_scale;
+    a.N = n_out;
+    a.Y = y;
+    a.y_vec = (n_out % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 8 == 0) ? 1 : 0;
+    return DPSGD_OK;
+}
+
+void i8_set_a(I8Args& a, const uint16_t* a_in, float tau) {
+    a.A = a_in;
+    a.tau = tau;
+    a.tau_on = (tau > 0.f && !std::isinf(tau)) ? 1 : 0;
+    a.a_vec = (a.K % 8 == 0 && reinterpret_cast<uintptr_t>(a_in) % 16 == 0) ? 1 : 0;
+}
+
+}  // namespace
+
+int dpsgd_i8_route(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_records,
+                   const uint16_t* a_in, int64_t k, float tau, void* stream) {
+    I8Args a;
+    if (int rc = i8_args(p, ws, n_rows, n_records, k, a)) return rc;
+    if (int rc = i8_check_a(a, a_in, tau)) return rc;
+    i8_set_a(a, a_in, tau);
+    hipError_t e = launch_i8_route(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "int8 routing launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_i8_matmul(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_records,
+                    const uint16_t* a_in, int64_t k, const int8_t* wq, const float* w_scale,
+                    int64_t n_out, uint16_t* y, void* stream) {
+    I8Args a;
+    if (int rc = i8_args(p, ws, n_rows, n_records, k, a)) return rc;
+    if (int rc = i8_check_a(a, a_in, 6.0f)) return rc;
+    if (int rc = i8_check_w(a, wq, w_scale, n_out, y)) return rc;
+    i8_set_a(a, a_in, 6.0f);
+    hipError_t e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 256 ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "int8 gemm launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_i8_forward(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_records,
+                     const uint16_t* a_in, int64_t k, const int8_t* wq, const float* w_scale,
+                     int64_t n_out, float tau, uint16_t* y, void* stream) {
+    I8Args a;
+    if (int rc = i8_args(p, ws, n_rows, n_records, k, a)) return rc;
+    if (int rc = i8_check_a(a, a_in, tau)) return rc;
+    if (int rc = i8_check_w(a, wq, w_scale, n_out, y)) return rc;
+    i8_set_a(a, a_in, tau);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_i8_route(a, s);
+    if (e != hipSuccess) return hip_fail(e, "int8 routing launch");
+    e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 256 ? 1 : 0, s);
+    if (e != hipSuccess) return hip_fail(e, "int8 gemm launch");
+    return DPSGD_OK;
+}
+
+int dpsgd_i8_intermediates(const dpsgd_i8_plan* p, const void* ws, int64_t n_rows, int64_t n_records,
+                           int64_t k, int8_t* q, float* row_scale, uint32_t* outlier_mask,
+                           int32_t* owner, void* stream) {
+    I8Args a;
+    if (int rc = i8_args(p, const_cast<void*>(ws), n_rows, n_records, k, a)) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    struct Part { void* dst; const void* src; int64_t bytes; } parts[] = {
+        {q, a.Q, n_rows * a.Kp},
+        {row_scale, a.s, n_rows * 4},
+        {outlier_mask, a.omask, n_records * a.KW * 4},
+        {owner, a.own, n_rows * 4},
+    };
+    for (const Part& pt : parts) {
+        if (!pt.dst || pt.bytes == 0) continue;
+        hipError_t e = hipMemcpyAsync(pt.dst, pt.src, (size_t)pt.bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "intermediates copy");
+    }
+    return DPSGD_OK;
+}
+
 
 const char* dpsgd_error_string(int code) {
     switch (code) {

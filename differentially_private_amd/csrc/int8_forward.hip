@@ -1,0 +1,462 @@
+// Record-owned LLM.int8 forward of one frozen linear layer ("Sensitivity Inflation from
+// Cross-Record Precision Routing in Private Quantized Fine-Tuning", Sec. 4.2, Eq. 6 and
+// Algorithm 1; the LLM.int8 decomposition as its Sec. 2 describes it).
+//
+// Four launches per layer:
+//   k_i8_clear  zero the per-record outlier masks;
+//   k_i8_scan   per row: its owner record, the row scale s_i = max |a| over the entries below
+//               tau, and the per-entry test |a| >= tau OR-ed into the owner's mask (a segmented
+//               reduction by atomics; masks are bit sets of K bits per record);
+//   k_i8_quant  per row: codes round(127 a / s_i), zero in the owner's outlier columns;
+//   k_i8_gemm   Y = fp16(dq16 + corr16): the exact integer product of the codes with the INT8
+//               weight on MFMA (v_mfma_i32_16x16x64_i8), dequantised in the epilogue, plus the
+//               FP16 correction of each row over its own record's outlier columns only.
+// Row-wise weight quantisation (k_i8_weight) runs once per frozen weight.
+//
+// Rounding (identical IEEE fp32 operations on both sides of every parity test): codes are
+// rint(fl(127 a) / s) with a correctly rounded division (fl(127 a) is exact), code 0 where s = 0;
+// dq16 = fp16(fl(fl(float(acc) * fl(s_i / 127)) * fl(s_W / 127))); the dequantised weight is
+// fp16(fl(float(code) * fl(s_W / 127))); the correction sums the exact products a * w in fp32
+// in ascending column order and rounds once to fp16; the two fp16 halves are added and rounded.
+//
+// The GEMM tile takes the union of the outlier columns of the records its rows belong to, but
+// every row multiplies only the columns in its own record's set (the others contribute exact
+// zeros, which leave an fp32 sum unchanged), so another record's outliers never change a row's
+// arithmetic.
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace dpsgd {
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint16_t f2h(float x) {   // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// fp16 of an fp32 result that must be rounded to fp32 first.  Without the empty asm the compiler
+// merges the producing multiply or FMA and the conversion into one mixed-precision FMA
+// (v_fma_mixlo_f16) that rounds the exact result to fp16 once; that differs from the two
+// roundings whenever the fp32 value lands on an fp16 tie (the contraction flags do not stop it).
+__device__ __forceinline__ uint16_t f2h_rounded(float x) {
+    asm volatile("" : "+v"(x));
+    return f2h(x);
+}
+
+__device__ __forceinline__ float div_rn(float x, float y) { return __fdiv_rn(x, y); }
+
+__device__ __forceinline__ int code_of(float a, float s) {
+    return s == 0.f ? 0 : (int)rintf(div_rn(127.f * a, s));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_i8_clear(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+// One wavefront per row (4 rows per workgroup).
+__global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.n) return;
+    // owner: the last record whose first row is <= row (empty records share a first row with
+    // the next one, so the last of them is the non-empty owner)
+    int64_t lo = 0, hi = a.n_rec - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (a.offsets[mid] <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    if (lane == 0) a.own[row] = (int32_t)lo;
+    const uint16_t* x = a.A + row * a.K;
+    uint32_t* om = a.omask + lo * a.KW;
+    const bool on = a.tau_on != 0;
+    const float tau = a.tau;
+    float mx = 0.f;
+    if (a.a_vec) {
+        for (int64_t c = lane; c < a.K / 8; c += 64) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
+            uint32_t bits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = fabsf(h2f(v[e >> 1] >> (16 * (e & 1))));
+                const bool o = on && f >= tau;
+                bits |= (uint32_t)o << e;
+                mx = o ? mx : fmaxf(mx, f);
+            }
+            if (bits) atomicOr(om + (8 * c) / 32, bits << ((8 * c) % 32));
+        }
+    } else {
+        for (int64_t j = lane; j < a.K; j += 64) {
+            const float f = fabsf(h2f(x[j]));
+            const bool o = on && f >= tau;
+            if (o) atomicOr(om + j / 32, 1u << (j % 32));
+            else mx = fmaxf(mx, f);
+        }
+    }
+    mx = wave_max(mx);
+    if (lane == 0) a.s[row] = mx;
+}
+
+// One wavefront per row: codes of the row in Q (pitch Kp bytes, zero past K).
+__global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.n) return;
+    const uint16_t* x = a.A + row * a.K;
+    const uint32_t* om = a.omask + (int64_t)a.own[row] * a.KW;
+    const float s = a.s[row];
+    int8_t* q = a.Q + row * a.Kp;
+    if (a.a_vec) {
+        for (int64_t c = lane; c < a.Kp / 8; c += 64) {
+            uint32_t lo = 0, hi = 0;
+            if (8 * c < a.K) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
+                const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = h2f(v[e >> 1] >> (16 * (e & 1)));
+                    const int code = ((m >> e) & 1u) ? 0 : code_of(f, s);
+                    const uint32_t b = (uint32_t)(code & 0xFF) << (8 * (e & 3));
+                    if (e < 4) lo |= b;
+                    else hi |= b;
+                }
+            }
+            *reinterpret_cast<uint2*>(q + 8 * c) = make_uint2(lo, hi);
+        }
+    } else {
+        for (int64_t j = lane; j < a.Kp; j += 64) {
+            int code = 0;
+            if (j < a.K && !((om[j / 32] >> (j % 32)) & 1u)) code = code_of(h2f(x[j]), s);
+            q[j] = (int8_t)code;
+        }
+    }
+}
+
+// One wavefront per output feature: s_W = max |w|, codes round(127 w / s_W) (pitch Kp).
+__global__ __launch_bounds__(256) void k_i8_weight(const uint16_t* __restrict__ W, int64_t N,
+                                                   int64_t K, int64_t Kp, int8_t* __restrict__ Wq,
+                                                   float* __restrict__ sW) {
+    const int lane = threadIdx.x & 63;
+    const int64_t o = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (o >= N) return;
+    const uint16_t* w = W + o * K;
+    float mx = 0.f;
+    for (int64_t j = lane; j < K; j += 64) mx = fmaxf(mx, fabsf(h2f(w[j])));
+    mx = wave_max(mx);
+    int8_t* q = Wq + o * Kp;
+    for (int64_t j = lane; j < Kp; j += 64) q[j] = (int8_t)(j < K ? code_of(h2f(w[j]), mx) : 0);
+    if (lane == 0) sW[o] = mx;
+}
+
+namespace {
+
+constexpr int kStages = 3;
+constexpr int kUC = 32;           // union columns staged per correction chunk
+constexpr int kRS = kUC + 4;      // row stride (floats) of the staged residual
+
+// Byte offset of 16-byte chunk c (0..3) of row r inside a staged k-step (rows of 64 bytes):
+// the chunk index is XOR-ed with bits 2-3 of the row, so the 16 rows read by one MFMA operand
+// load spread over all 64 LDS banks.
+__device__ __forceinline__ uint32_t stage_off(int r, int c) {
+    return (uint32_t)(r * 64 + 16 * (c ^ ((r >> 2) & 3)));
+}
+
+}  // namespace
+
+// Workgroup tile: BI = 16 FI WI rows (i) x BO = 16 FO WO output features (o); WI x WO
+// wavefronts of (16 FI) x (16 FO).  MFMA operand a = weight rows (o), b = code rows (i): lane l
+// of a 16x16 result holds row i = l % 16 and the four features 4 (l / 16) .. + 3, so the fp16
+// output is written 8 bytes per lane.
+template <int FI, int FO, int WI, int WO>
+__global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
+    constexpr int NW = WI * WO, NT = 64 * NW;
+    constexpr int BI = 16 * FI * WI, BO = 16 * FO * WO;
+    constexpr int STAGE = (BI + BO) * 64;
+    constexpr int CQ = BI / 16 / NW, CW = BO / 16 / NW;   // copies per wave per k-step
+    static_assert(CQ * 16 * NW == BI && CW * 16 * NW == BO, "copy split");
+    constexpr int EPI = (BI + BI + BO + kI8MaxKW + kUC + 16) * 4 + (BI * kRS + kUC * BO) * 4;
+    constexpr int LDS = kStages * STAGE > EPI ? kStages * STAGE : EPI;
+    __shared__ __attribute__((aligned(16))) char lds[LDS];
+
+    const int64_t n = a.n, N = a.N;
+    int ti, to;
+    if (!tile_of((int)((n + BI - 1) / BI), (int)((N + BO - 1) / BO), 4, ti, to)) return;
+    const int64_t i0 = (int64_t)ti * BI, o0 = (int64_t)to * BO;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wi = w % WI, wo = w / WI;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    // copies: copy q of a k-step moves rows 16 q .. 16 q + 15 of the code tile (or the weight
+    // tile), 64 bytes each; lane L lands at 16 L, i.e. row 16 q + L / 4, stored chunk L % 4,
+    // which holds logical chunk (L % 4) ^ ((L / 16) % 4).  Rows past the end re-read the last row.
+    uint32_t offq[CQ], offw[CW];
+#pragma unroll
+    for (int q = 0; q < CQ; ++q) {
+        const int64_t r = std::min<int64_t>(i0 + 16 * (CQ * w + q) + (lane >> 2), n - 1);
+        offq[q] = (uint32_t)(r * a.Kp + 16 * ((lane & 3) ^ (g & 3)));
+    }
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+        const int64_t r = std::min<int64_t>(o0 + 16 * (CW * w + q) + (lane >> 2), N - 1);
+        offw[q] = (uint32_t)(r * a.Kp + 16 * ((lane & 3) ^ (g & 3)));
+    }
+    // operand reads: lane l reads row l % 16 of a 16-row block, logical chunk l / 16
+    const uint32_t rd_w = (uint32_t)(BI * 64) + stage_off(16 * FO * wo + l16, g);
+    const uint32_t rd_q = stage_off(16 * FI * wi + l16, g);
+
+    const char* baseq = reinterpret_cast<const char*>(a.Q);
+    const char* basew = reinterpret_cast<const char*>(a.Wq);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    auto issue = [&](int64_t s, int st) {
+        const char* pq = baseq + 64 * s;
+        const char* pw = basew + 64 * s;
+        const uint32_t dst = lds0 + (uint32_t)(st * STAGE);
+#pragma unroll
+        for (int q = 0; q < CQ; ++q) copy16(pq, offq[q], dst + (uint32_t)(CQ * w + q) * 1024u);
+#pragma unroll
+        for (int q = 0; q < CW; ++q)
+            copy16(pw, offw[q], dst + (uint32_t)(BI * 64 + (CW * w + q) * 1024));
+    };
+
+    i32x4 acc[FO][FI];
+#pragma unroll
+    for (int f = 0; f < FO; ++f)
+#pragma unroll
+        for (int e = 0; e < FI; ++e) acc[f][e] = i32x4{0, 0, 0, 0};
+
+    const int64_t total = a.Kp / 64;
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k)
+        if (k < total) issue(k, k);
+    int st = 0, stn = kStages - 1;
+    for (int64_t s = 0; s < total; ++s) {
+        // this wave's copies of step s are done once at most the later issued steps are in
+        // flight; the barrier publishes all waves' copies and retires step s - 1's stage
+        wait_copies<CQ + CW>(std::min<int64_t>(s + kStages - 2, total - 1) - s);
+        __syncthreads();
+        if (s + kStages - 1 < total) issue(s + kStages - 1, stn);
+        const char* S = lds + st * STAGE;
+        i32x4 bq[FI];
+#pragma unroll
+        for (int e = 0; e < FI; ++e) bq[e] = *reinterpret_cast<const i32x4*>(S + rd_q + e * 1024);
+#pragma unroll
+        for (int f = 0; f < FO; ++f) {
+            const i32x4 aw = *reinterpret_cast<const i32x4*>(S + rd_w + f * 1024);
+#pragma unroll
+            for (int e = 0; e < FI; ++e)
+                acc[f][e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw, bq[e], acc[f][e], 0, 0, 0);
+        }
+        st = st == kStages - 1 ? 0 : st + 1;
+        stn = stn == kStages - 1 ? 0 : stn + 1;
+    }
+    __syncthreads();   // every wave is done with the stages: the epilogue reuses the LDS
+
+    int* own_t = reinterpret_cast<int*>(lds);          // owner record of each tile row (-1 past n)
+    float* sat = reinterpret_cast<float*>(own_t + BI);  // fl(s_i / 127)
+    float* sbt = sat + BI;                              // fl(s_W / 127)
+    uint32_t* tmask = reinterpret_cast<uint32_t*>(sbt + BO);   // union of the rows' record sets
+    int* cols = reinterpret_cast<int*>(tmask + kI8MaxKW);      // columns of the current chunk
+    int* wsum = cols + kUC;                                    // scan scratch (NW + 1)
+    float* Rt = reinterpret_cast<float*>(wsum + 16);           // [BI][kRS] residual a or 0
+    float* Wt = Rt + BI * kRS;                                 // [kUC][BO] dequantised weight
+    for (int t = tid; t < BI; t += NT) {
+        const int64_t r = i0 + t;
+        own_t[t] = r < n ? a.own[r] : -1;
+        sat[t] = r < n ? div_rn(a.s[r], 127.f) : 0.f;
+    }
+    for (int t = tid; t < BO; t += NT) {
+        const int64_t o = o0 + t;
+        sbt[t] = o < N ? div_rn(a.sW[o], 127.f) : 0.f;
+    }
+    __syncthreads();
+
+    // FP16 correction over the union of the tile's record sets, in chunks of kUC columns
+    const int rows_valid = (int)std::min<int64_t>(BI, n - i0);
+    const int r_lo = own_t[0], r_hi = own_t[rows_valid - 1];
+    const int KW = (int)a.KW;
+    for (int wd = tid; wd < KW; wd += NT) {
+        uint32_t m = 0;
+        for (int r = r_lo; r <= r_hi; ++r) m |= a.omask[(int64_t)r * KW + wd];
+        tmask[wd] = m;
+    }
+    __syncthreads();
+    // rank of each thread's first union column: thread t owns words [t WPT, t WPT + WPT)
+    constexpr int WPT = (kI8MaxKW + NT - 1) / NT;
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+        const int wd = tid * WPT + k;
+        if (wd < KW) mine += __popc(tmask[wd]);
+    }
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = incl - mine, nu = 0;
+    for (int k = 0; k < NW; ++k) {
+        if (k < w) base += wsum[k];
+        nu += wsum[k];
+    }
+    const int n_chunks = (nu + kUC - 1) / kUC;
+
+    // stage union columns c0 .. c0 + kUC - 1: Rt[i][u] = a (row i's own outlier column) or 0,
+    // Wt[u][o] = the dequantised weight
+    auto stage = [&](int c0) {
+        const int nuc = std::min(kUC, nu - c0);
+        __syncthreads();   // the previous chunk's staged values are consumed
+        int rank = base;
+        for (int k = 0; k < WPT; ++k) {
+            const int wd = tid * WPT + k;
+            if (wd >= KW) break;
+            uint32_t m = tmask[wd];
+            while (m) {
+                const int b = __builtin_ctz(m);
+                m &= m - 1;
+                if (rank >= c0 && rank < c0 + kUC) cols[rank - c0] = 32 * wd + b;
+                ++rank;
+            }
+        }
+        __syncthreads();
+        for (int t = tid; t < BI * kUC; t += NT) {
+            const int il = t / kUC, u = t % kUC;
+            float v = 0.f;
+            if (u < nuc && il < rows_valid) {
+                const int col = cols[u];
+                const int r = own_t[il];
+                if ((a.omask[(int64_t)r * KW + col / 32] >> (col % 32)) & 1u)
+                    v = h2f(a.A[(i0 + il) * a.K + col]);
+            }
+            Rt[il * kRS + u] = v;
+        }
+        for (int t = tid; t < kUC * BO; t += NT) {
+            const int u = t / BO, ol = t % BO;
+            float v = 0.f;
+            if (u < nuc && o0 + ol < N)
+                v = h2f(f2h_rounded((float)a.Wq[(o0 + ol) * a.Kp + cols[u]] * sbt[ol]));
+            Wt[u * BO + ol] = v;
+        }
+        __syncthreads();
+    };
+    if (n_chunks == 1) stage(0);
+
+    // one 16-row group at a time: correction (fp32, ascending columns), then
+    // Y = fp16(dq16 + corr16) with dq16 = fp16(fl(fl(float(acc) * fl(s_i/127)) * fl(s_W/127)))
+#pragma unroll
+    for (int e = 0; e < FI; ++e) {
+        const int il = 16 * FI * wi + 16 * e + l16;
+        f4 corr[FO];
+#pragma unroll
+        for (int f = 0; f < FO; ++f) corr[f] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < n_chunks; ++ch) {
+            if (n_chunks > 1) stage(ch * kUC);
+            const int nuc = std::min(kUC, nu - ch * kUC);
+            const float* rrow = Rt + il * kRS;
+            for (int u = 0; u < nuc; u += 4) {
+                const f4 rv = *reinterpret_cast<const f4*>(rrow + u);
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu) {
+                    if (u + uu >= nuc) break;
+#pragma unroll
+                    for (int f = 0; f < FO; ++f) {
+                        const f4 wv = *reinterpret_cast<const f4*>(
+                            Wt + (u + uu) * BO + 16 * FO * wo + 16 * f + 4 * g);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) corr[f][r] = fmaf(rv[uu], wv[r], corr[f][r]);
+                    }
+                }
+            }
+        }
+        const int64_t i = i0 + il;
+        const float sa = sat[il];
+#pragma unroll
+        for (int f = 0; f < FO; ++f) {
+            const int obl = 16 * FO * wo + 16 * f + 4 * g;
+            const int64_t ob = o0 + obl;
+            uint16_t y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float d = h2f(f2h_rounded(((float)acc[f][e][r] * sa) * sbt[obl + r]));
+                const float c = h2f(f2h_rounded(corr[f][r]));
+                y[r] = f2h(d + c);
+            }
+            if (i >= n) continue;
+            uint16_t* dst = a.Y + i * N + ob;
+            if (a.y_vec && ob + 4 <= N) {
+                *reinterpret_cast<uint2*>(dst) =
+                    make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ob + r < N) dst[r] = y[r];
+            }
+        }
+    }
+}
+
+namespace {
+
+template <int FI, int FO, int WI, int WO>
+void launch_gemm(const I8Args& a, hipStream_t s) {
+    constexpr int BI = 16 * FI * WI, BO = 16 * FO * WO;
+    const int64_t tiles = ((a.n + BI - 1) / BI) * ((a.N + BO - 1) / BO);
+    hipLaunchKernelGGL((k_i8_gemm<FI, FO, WI, WO>), dim3((unsigned)tiles), dim3(64 * WI * WO), 0, s, a);
+}
+
+}  // namespace
+
+int64_t i8_tiles(int64_t n, int64_t N, int big) {
+    const int64_t b = big ? 256 : 128;
+    return ((n + b - 1) / b) * ((N + b - 1) / b);
+}
+
+hipError_t launch_i8_route(const I8Args& a, hipStream_t s) {
+    const int64_t words = a.n_rec * a.KW;
+    if (words > 0)
+        hipLaunchKernelGGL(k_i8_clear, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)),
+                           dim3(256), 0, s, a.omask, words);
+    if (a.n > 0) {
+        const unsigned g = (unsigned)((a.n + 3) / 4);
+        hipLaunchKernelGGL(k_i8_scan, dim3(g), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_i8_quant, dim3(g), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_i8_gemm(const I8Args& a, int big, hipStream_t s) {
+    if (a.n > 0 && a.N > 0) {
+        if (big) launch_gemm<4, 8, 4, 2>(a, s);
+        else launch_gemm<4, 4, 2, 2>(a, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_i8_weight(const uint16_t* W, int64_t N, int64_t K, int64_t Kp, int8_t* Wq,
+                            float* sW, hipStream_t s) {
+    if (N > 0) hipLaunchKernelGGL(k_i8_weight, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, Kp, Wq, sW);
+    return hipGetLastError();
+}
+
+}  // namespace dpsgd

@@ -248,6 +248,86 @@ int dpsgd_rdp_to_epsilon(const double* orders, const double* rdp, int32_t n_orde
 int dpsgd_gaussian_pair_delta(double eps, double mu, double* delta_out);
 int dpsgd_gaussian_pair_epsilon(double delta, double mu, double* eps_out);
 
+/* ---- Record-owned LLM.int8 forward of a frozen linear layer ----
+ * ("Sensitivity Inflation from Cross-Record Precision Routing in Private
+ * Quantized Fine-Tuning", Sec. 4.2, Eq. 6 and Algorithm 1; LLM.int8 as its
+ * Sec. 2 describes it.)  The upstream producer of a layer's activations on a
+ * quantised frozen backbone.  For n activation rows A (fp16, n x k, row-major,
+ * contiguous) owned by records (record r owns rows [offsets[r], offsets[r+1])):
+ *   M_ij = |A_ij| >= tau;  O_r = columns where a row of record r has M true;
+ *   s_i  = max |A_ij| over the entries with M_ij false (0 if none);
+ *   Q_ij = round(127 A_ij / s_i), ties to even, 0 if j in O_owner(i) or s_i = 0;
+ *   Y_i  = fp16(dq16 + corr16), where
+ *     dq16   = fp16(fl(fl(float(Q_i . Wq_o) * fl(s_i/127)) * fl(s_W,o/127))),
+ *     corr16 = fp16(sum over j in O_owner(i), ascending, in fp32, of
+ *              A_ij * What_oj), What_oj = fp16(fl(float(Wq_oj) * fl(s_W,o/127))).
+ * Every row multiplies only its own record's outlier columns, so a record's
+ * output does not depend on the other records of the physical batch.  Batched
+ * LLM.int8 (one outlier set for all rows) is the case of a single record
+ * spanning all rows.  tau <= 0 or +inf: no outlier path (threshold zero).
+ * Non-finite activations give unspecified (but in-bounds) results.
+ *
+ * Weights: Wq is [n_out, pitch(k)] int8 (row-wise codes, zero past k) with one
+ * scale s_W per output feature (the row's max |w|), as written by
+ * dpsgd_i8_quantize_weight.  Y is [n, n_out] fp16, row-major.  The plan is a
+ * host object with the capacities; its workspace (device, 256-byte aligned,
+ * dpsgd_i8_plan_create's ws_bytes) holds the record offsets, owners, row
+ * scales, outlier masks and codes of the current batch.  Argument errors are
+ * returned before any launch. */
+typedef struct dpsgd_i8_plan dpsgd_i8_plan;
+
+/* Bytes per INT8 code row: k rounded up to a multiple of 64 (0 unless
+ * 1 <= k <= 32768). */
+int64_t dpsgd_i8_pitch(int64_t k);
+
+/* Capacities: at most max_rows activation rows (max_rows * pitch(max_k)
+ * < 2^31), max_records >= 1 records, 1 <= max_k <= 32768 columns. */
+int dpsgd_i8_plan_create(int64_t max_rows, int64_t max_records, int64_t max_k, dpsgd_i8_plan** out,
+                         size_t* ws_bytes);
+void dpsgd_i8_plan_destroy(dpsgd_i8_plan* plan);
+
+/* Row-wise quantisation of a frozen fp16 weight W [n_out, k] (device, row-major):
+ * w_scale[o] = max_j |W_oj| (float32), wq[o][j] = round(127 W_oj / w_scale[o])
+ * (ties to even, 0 where the scale is 0; zero for j in [k, pitch(k))).
+ * wq: device, n_out x pitch(k) bytes, 16-byte aligned. */
+int dpsgd_i8_quantize_weight(const uint16_t* w, int64_t n_out, int64_t k, int8_t* wq, float* w_scale,
+                             void* stream);
+
+/* Record offsets of the current physical batch (host array of n_records + 1
+ * entries: offsets[0] = 0, non-decreasing, offsets[n_records] <= max_rows;
+ * empty records allowed), copied stream-ordered into `ws` (the host array may
+ * be reused on return).  Every following dpsgd_i8_forward on this workspace
+ * must pass n_rows = offsets[n_records] and the same n_records. */
+int dpsgd_i8_set_records(const dpsgd_i8_plan* plan, void* ws, const int64_t* offsets, int64_t n_records,
+                         void* stream);
+
+/* Y = record-owned INT8 forward of the n_rows x k activations `a` (device fp16)
+ * through (wq, w_scale) (n_out output features).  tau: the outlier threshold
+ * (6 in LLM.int8's default; NaN is rejected).  Four launches; the workspace
+ * keeps this call's intermediates until the next call. */
+int dpsgd_i8_forward(const dpsgd_i8_plan* plan, void* ws, int64_t n_rows, int64_t n_records,
+                     const uint16_t* a, int64_t k, const int8_t* wq, const float* w_scale,
+                     int64_t n_out, float tau, uint16_t* y, void* stream);
+
+/* The two halves of dpsgd_i8_forward, for callers that time or overlap them:
+ * dpsgd_i8_route runs Algorithm 1's steps 1-6 (masks, owners, row scales,
+ * codes) into the workspace; dpsgd_i8_matmul runs step 7 (the INT8 product,
+ * dequantisation and the per-record FP16 correction) and must follow a route
+ * of the same activations (same a, k, n_rows, n_records) on this workspace. */
+int dpsgd_i8_route(const dpsgd_i8_plan* plan, void* ws, int64_t n_rows, int64_t n_records,
+                   const uint16_t* a, int64_t k, float tau, void* stream);
+int dpsgd_i8_matmul(const dpsgd_i8_plan* plan, void* ws, int64_t n_rows, int64_t n_records,
+                    const uint16_t* a, int64_t k, const int8_t* wq, const float* w_scale,
+                    int64_t n_out, uint16_t* y, void* stream);
+
+/* Copies of the last forward's intermediates (device destinations, each
+ * optional): q [n_rows, pitch(k)] int8 codes, row_scale [n_rows] float32,
+ * outlier_mask [n_records, ceil(k/32)] uint32 (bit j % 32 of word j / 32 set
+ * iff column j is in O_r), owner [n_rows] int32. */
+int dpsgd_i8_intermediates(const dpsgd_i8_plan* plan, const void* ws, int64_t n_rows, int64_t n_records,
+                           int64_t k, int8_t* q, float* row_scale, uint32_t* outlier_mask,
+                           int32_t* owner, void* stream);
+
 /* Synchronise `stream` and read the status word: DPSGD_OK or
  * DPSGD_ERR_NONFINITE (or DPSGD_ERR_HIP). */
 int dpsgd_status(const dpsgd_plan* plan, const void* ws, void* stream);

@@ -134,11 +134,13 @@ def forward(A: np.ndarray, offsets, Wq: np.ndarray, sW: np.ndarray, tau: float,
     Q = quant_codes(A, s)                                         # step 5
     Q[row_set] = 0
     R = np.where(row_set, A, F16(0))                              # step 6
-    # step 7, INT8 part: the exact integer product, then the two dequantisation scales
-    acc = Q.astype(np.int64) @ Wq.astype(np.int64).T
+    # step 7, INT8 part: the exact integer product (in fp64: every partial sum is an integer of
+    # magnitude <= 127^2 K < 2^53, so any summation order is exact), then the dequantisation
+    acc = np.rint(Q.astype(np.float64) @ Wq.astype(np.float64).T).astype(np.int64)
     sa = s.astype(F32) / F32(127)
     sb = sW.astype(F32) / F32(127)
-    dq16 = ((acc.astype(F32) * sa[:, None]) * sb[None, :]).astype(F16)
+    with np.errstate(over="ignore"):        # fp16 overflow rounds to inf (IEEE)
+        dq16 = ((acc.astype(F32) * sa[:, None]) * sb[None, :]).astype(F16)
     # step 7, FP16 part: each row over its own outlier columns, ascending, fp32 accumulation
     What = dequant_weight(Wq, sW)
     corr = np.zeros((n, N), dtype=F32)
@@ -151,8 +153,9 @@ def forward(A: np.ndarray, offsets, Wq: np.ndarray, sW: np.ndarray, tau: float,
         for j in cols:
             corr[lo:hi] = corr[lo:hi] + (R[lo:hi, j].astype(F32)[:, None] *
                                          What[:, j].astype(F32)[None, :])
-    corr16 = corr.astype(F16)
-    Y = (dq16.astype(F32) + corr16.astype(F32)).astype(F16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        corr16 = corr.astype(F16)
+        Y = (dq16.astype(F32) + corr16.astype(F32)).astype(F16)
     return {"M": M, "O": O, "U": U, "s": s, "Q": Q, "R": R, "acc": acc, "dq16": dq16,
             "corr16": corr16, "Y": Y}
 

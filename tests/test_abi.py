@@ -203,3 +203,37 @@ def test_unknown_plan_flags_rejected():
     desc = dp.PlanDesc(1, layers, dp.DTYPE_F32, 4, 4, dp.PATH_AUTO, dp.SUM_AUTO, 2)
     h, ws = ctypes.c_void_p(), ctypes.c_size_t()
     assert lib.dpsgd_plan_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws)) == dp.ERR_INVALID_ARG
+
+
+def test_i8_entry_points_reject_before_launch():
+    """The INT8 forward's argument errors are returned on the host (no GPU is touched)."""
+    lib = dp.load()
+    assert dp.i8_pitch(4) == 64 and dp.i8_pitch(768) == 768 and dp.i8_pitch(770) == 832
+    assert dp.i8_pitch(0) == 0 and dp.i8_pitch(32769) == 0
+    for args in [(-1, 1, 8), (8, 0, 8), (8, 1, 0), (8, 1, 32769), (1 << 20, 1, 4096)]:
+        with pytest.raises(dp.DpsgdError) as e:
+            dp.I8Plan(*args)
+        assert e.value.code == dp.ERR_INVALID_ARG
+    plan = dp.I8Plan(64, 4, 128)
+    assert plan.ws_bytes > 64 * 128
+    fake_ws = 1 << 40          # never dereferenced: every case below fails validation first
+    bad_offsets = [[1, 4], [0, 5, 3], [0, 65], [0] * 6]
+    for off in bad_offsets:
+        with pytest.raises(dp.DpsgdError):
+            dp.i8_set_records(plan, fake_ws, off, stream=0)
+    ok = dict(n_rows=8, n_records=2, A=fake_ws, k=64, wq=fake_ws, w_scale=fake_ws, n_out=16,
+              tau=6.0, Y=fake_ws, stream=0)
+    for change in [dict(n_rows=65), dict(n_records=5), dict(n_records=0), dict(k=129), dict(k=0),
+                   dict(tau=float("nan")), dict(A=0), dict(wq=0), dict(Y=0), dict(wq=fake_ws + 8),
+                   dict(n_out=-1)]:
+        kw = dict(ok, **change)
+        with pytest.raises(dp.DpsgdError) as e:
+            dp.i8_forward(plan, fake_ws + (1 if change == {} else 0), **kw)
+        assert e.value.code == dp.ERR_INVALID_ARG
+    with pytest.raises(dp.DpsgdError):
+        dp.i8_forward(plan, fake_ws + 16, **ok)       # misaligned workspace
+    for args in [(fake_ws, 4, 0, fake_ws, fake_ws), (fake_ws, -1, 8, fake_ws, fake_ws),
+                 (0, 4, 8, fake_ws, fake_ws)]:
+        with pytest.raises(dp.DpsgdError):
+            dp.i8_quantize_weight(*args, stream=0)
+    assert lib.dpsgd_i8_pitch(64) == 64

@@ -270,3 +270,18 @@ def test_threshold_is_inclusive():
     assert r["O"][:, 0].tolist() == [True, False, True]
     assert r["Q"][1, 0] == 127 and r["Q"][0, 0] == 0 and r["Q"][2, 0] == 0
     assert r["Y"][0, 0] == 6.0 and r["Y"][2, 0] == -6.0
+
+
+def test_integer_product_is_exact():
+    """The INT8 accumulator equals the int64 product of the codes at the largest K (32768) with
+    every code at +-127 (the extreme partial sums)."""
+    rng = np.random.default_rng(13)
+    K = 32768
+    Q = rng.choice(np.array([-127, 127], dtype=np.int8), (3, K))
+    Wq = rng.choice(np.array([-127, 127], dtype=np.int8), (2, K))
+    Wq[0] = Q[0]
+    A = (Q.astype(np.float32) / 64).astype(F16)          # row scale 127/64: codes are Q
+    r = o8.forward(A, [0, 3], Wq, np.full(2, 127 / 64, dtype=np.float32), 6.0)
+    assert np.array_equal(r["Q"], Q)
+    assert np.array_equal(r["acc"], Q.astype(np.int64) @ Wq.astype(np.int64).T)
+    assert r["acc"][0, 0] == 127 * 127 * K
