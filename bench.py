@@ -340,6 +340,173 @@ def secondary(args, w, torch, dev, dp, datagen):
     print(json.dumps(line), flush=True)
 
 
+I8_PEAK_TOPS = 5000.0   # dense INT8 MFMA, ops/s x 1e-12
+
+
+def int8_model(torch, dev, dp, seed=0):
+    """The frozen OPT-125M backbone's 72 INT8 layers (12 blocks x q, k, v, out: 768 -> 768, fc1:
+    768 -> 3072, fc2: 3072 -> 768) over one physical batch of B = 16 records x T = 256 tokens.
+    q, k and v read the same input: their frozen weights are stacked into one 2304 x 768 weight
+    (row-wise codes and scales are per output feature, so every output is the one the separate
+    layers give), leaving four INT8 forwards per block.  Synthetic activations with three shared
+    outlier columns and record-owned ones (datagen.int8), weights ~ N(0, 0.02)."""
+    import numpy as np
+    from datagen import int8 as gen
+    B, T, H, F = 16, 256, 768, 3072
+    offsets = gen.lengths_offsets([T] * B)
+    n = int(offsets[-1])
+    layers = []
+    for blk in range(12):
+        for j, (K, N, n_proj) in enumerate(((H, H, 3), (H, H, 1), (H, F, 1), (F, H, 1))):
+            A, _, _, _ = gen.activations(1000 * seed + 10 * blk + j, [T] * B, K)
+            W = np.concatenate([gen.weights(100 * blk + 10 * j + p, N, K) for p in range(n_proj)])
+            W = torch.from_numpy(W).to(dev)
+            Nt = N * n_proj
+            wq = torch.empty((Nt, dp.i8_pitch(K)), dtype=torch.int8, device=dev)
+            sw = torch.empty(Nt, dtype=torch.float32, device=dev)
+            dp.i8_quantize_weight(W, Nt, K, wq, sw)
+            del W
+            Y = torch.empty((n, Nt), dtype=torch.float16, device=dev)
+            layers.append({"A": torch.from_numpy(A).to(dev), "K": K, "N": Nt, "wq": wq, "sw": sw,
+                           "Y": Y, "projections": n_proj})
+    torch.cuda.synchronize()
+    return {"B": B, "T": T, "n": n, "offsets": offsets, "layers": layers}
+
+
+def int8_line(args, torch, dev, dp):
+    """Record-owned LLM.int8 forward of the OPT-125M backbone (72 INT8 layers, one physical batch
+    of 16 x 256 tokens per step): eager and HIP-graph timings of the whole forward, the GEMM's
+    roofline from HIP events around each dpsgd_i8_matmul, the batched LLM.int8 variant (one
+    record spanning the batch: the same kernels with the batch-wide union) for comparison, and
+    the oracle's rate on one layer of each shape."""
+    import ctypes
+    import numpy as np
+    m = int8_model(torch, dev, dp)
+    n, B = m["n"], m["B"]
+    plan = dp.I8Plan(n, B, 3072)
+    ws = plan.workspace(dev)
+    ws_b = plan.workspace(dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    lib = dp.load()
+    tau = ctypes.c_float(6.0)
+
+    def marshal(w, n_rec, st):
+        """The block's four INT8 forwards (qkv, out, fc1, fc2) as C calls."""
+        return [(lib.dpsgd_i8_forward, (plan.handle, w.data_ptr(), n, n_rec, L["A"].data_ptr(),
+                                        L["K"], L["wq"].data_ptr(), L["sw"].data_ptr(), L["N"],
+                                        tau, L["Y"].data_ptr(), st)) for L in m["layers"]]
+
+    calls = marshal(ws, B, sp)
+    calls_b = marshal(ws_b, 1, sp)
+    dp.i8_set_records(plan, ws, m["offsets"], stream)
+    dp.i8_set_records(plan, ws_b, [0, n], stream)
+
+    def forward(cs):
+        for f, c in cs:
+            rc = f(*c)
+            if rc:
+                dp._check(rc)
+
+    for _ in range(args.warmup):
+        forward(calls)
+        forward(calls_b)
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / reps
+
+    eager_ms = timed(lambda: (dp.i8_set_records(plan, ws, m["offsets"], stream), forward(calls)),
+                     args.steps)
+    batched_eager_ms = timed(lambda: forward(calls_b), args.steps)
+
+    # the same forward captured once into a HIP graph (record offsets set outside it)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forward(marshal(ws, B, torch.cuda.current_stream().cuda_stream))
+    gb = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gb):
+        forward(marshal(ws_b, 1, torch.cuda.current_stream().cuda_stream))
+    for _ in range(3):
+        g.replay()
+        gb.replay()
+    graph_ms = timed(g.replay, args.steps)
+    batched_graph_ms = timed(gb.replay, args.steps)
+
+    # dominant kernel: the INT8 GEMM of every layer, HIP events around dpsgd_i8_matmul (the
+    # routing kernels of that layer run untimed just before it)
+    ops = 0
+    gemm_ms = 0.0
+    reps = max(1, args.steps // 10)
+    launches = 0
+    for _ in range(reps):
+        for L in m["layers"]:
+            dp.i8_route(plan, ws, n, B, L["A"], L["K"], 6.0, stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dp.i8_matmul(plan, ws, n, B, L["A"], L["K"], L["wq"], L["sw"], L["N"], L["Y"], stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gemm_ms += e0.elapsed_time(e1)
+            ops += 2 * n * L["K"] * L["N"]
+            launches += 1
+    avg_ms = gemm_ms / launches
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": achieved / I8_PEAK_TOPS, "traffic": None,
+            "kernel": "k_i8_gemm (INT8 MFMA, dequantisation + record-owned FP16 correction)",
+            "algorithmic_ops_per_launch": ops / launches, "avg_ms": avg_ms, "launches": launches}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import int8_forward as o8      # host baseline only
+        per_shape = {}
+        t_start = time.perf_counter()
+        for K, N, count in ((768, 2304, 12), (768, 768, 12), (768, 3072, 12), (3072, 768, 12)):
+            L = next(x for x in m["layers"] if x["K"] == K and x["N"] == N)
+            A = L["A"].cpu().numpy()
+            W = np.random.default_rng(K + N).standard_normal((N, K)).astype(np.float16)
+            Wq, sW, _ = o8.quantize_weight(W)
+            t0 = time.perf_counter()
+            o8.forward(A, m["offsets"], Wq, sW, 6.0)
+            per_shape[(K, N)] = (time.perf_counter() - t0, count)
+        step_s = sum(t * c for t, c in per_shape.values())
+        try:
+            import threadpoolctl
+            threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
+        except Exception:
+            threads = os.cpu_count()
+        cpu = {"value": B / step_s, "unit": "records/s", "cores": threads, "kind": "oracle",
+               "sample": "one forward of each shape (qkv 768->2304, out 768->768, fc1 "
+                         "768->3072, fc2 3072->768) over the 16 x 256-token batch, times the 12 "
+                         "blocks "
+                         f"({time.perf_counter() - t_start:.1f} s wall; numpy, BLAS threads)"}
+
+    line = {"metric": "records/sec, record-owned LLM.int8 forward of a frozen backbone",
+            "value": B / (graph_ms * 1e-3), "unit": "records/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": graph_ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+            "data": "synthetic",
+            "config": {"workload": "opt125m_int8_forward", "int8_layers": 72,
+                       "forwards_per_step": len(m["layers"]), "qkv_fused": True,
+                       "records": B, "tokens": m["T"], "rows": n, "tau": 6.0,
+                       "timing": "HIP graph of the 48 forwards; record offsets set before"},
+            "roofline": roof, "cpu_baseline": cpu,
+            "eager_ms_per_step": eager_ms,
+            "batched_union": {"graph_ms_per_step": batched_graph_ms,
+                              "eager_ms_per_step": batched_eager_ms},
+            "tokens_per_s": n / (graph_ms * 1e-3)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,7 +520,7 @@ def main():
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--manifest", default=None, help="write a run manifest JSON here")
-    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy", "sample"],
+    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy", "sample", "int8"],
                     help="step: the benchmark; kernel: only the dominant kernel, --steps times "
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB "
                          "(the reference for scaling HBM byte counters)")
@@ -397,6 +564,8 @@ def main():
         return
     if args.mode == "sample":
         return sample_line(args, torch, dev, dp)
+    if args.mode == "int8":
+        return int8_line(args, torch, dev, dp)
     w = datagen.workload(args.workload)
     if args.mode == "step" and args.users:
         return users_line(args, w, torch, dev, dp, datagen)

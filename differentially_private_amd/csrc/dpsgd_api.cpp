@@ -519,7 +519,7 @@ bool all_stored(const dpsgd_plan* p) {
 // Host plan of the record-owned INT8 forward: capacities and the workspace layout.
 struct I8PlanImpl {
     int64_t max_rows, max_records, max_k, kp, kw;
-    int64_t off_offsets, off_own, off_s, off_omask, off_q, ws_bytes;
+    int64_t off_offsets, off_own, off_s, off_omask, off_pmask, off_q, ws_bytes;
 };
 
 int64_t i8_pitch(int64_t k) { return (k + 63) / 64 * 64; }
@@ -944,13 +944,15 @@ int dpsgd_i8_plan_create(int64_t max_rows, int64_t max_records, int64_t max_k, d
     p->kw = kw;
     int64_t off = 0;
     p->off_offsets = off;
-    off = align_up(off + (max_records + 1) * 8);
+    off = align_up(off + 2 * (max_records + 1) * 8);
     p->off_own = off;
     off = align_up(off + max_rows * 4);
     p->off_s = off;
     off = align_up(off + max_rows * 4);
     p->off_omask = off;
     off = align_up(off + max_records * kw * 4);
+    p->off_pmask = off;
+    off = align_up(off + i8_scan_blocks(max_rows, max_records) * kw * 4);
     p->off_q = off;
     off = align_up(off + max_rows * kp);
     p->ws_bytes = off;
@@ -971,9 +973,18 @@ int dpsgd_i8_set_records(const dpsgd_i8_plan* p, void* ws, const int64_t* offset
     for (int64_t r = 0; r < n_records; ++r)
         if (offsets[r + 1] < offsets[r]) return fail(DPSGD_ERR_INVALID_ARG, "offsets must be non-decreasing");
     if (offsets[n_records] > p->max_rows) return fail(DPSGD_ERR_INVALID_ARG, "offsets[n_records] exceeds max_rows");
-    hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_offsets, offsets,
-                                  (size_t)(n_records + 1) * sizeof(int64_t), hipMemcpyHostToDevice,
-                                  (hipStream_t)stream);
+    // row offsets, then the scan's block offsets (max(1, ceil(len / 16)) blocks per record)
+    std::vector<int64_t> h(2 * (size_t)(n_records + 1));
+    for (int64_t r = 0; r <= n_records; ++r) h[r] = offsets[r];
+    int64_t b = 0;
+    for (int64_t r = 0; r < n_records; ++r) {
+        h[n_records + 1 + r] = b;
+        b += std::max<int64_t>(1, (offsets[r + 1] - offsets[r] + 15) / 16);
+    }
+    h[2 * n_records + 1] = b;
+    char* w = static_cast<char*>(ws);
+    hipError_t e = hipMemcpyAsync(w + p->off_offsets, h.data(), h.size() * sizeof(int64_t),
+                                  hipMemcpyHostToDevice, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "record offsets copy");
     return DPSGD_OK;
 }
@@ -1008,6 +1019,7 @@ int i8_args(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_records,
     a.own = reinterpret_cast<int32_t*>(w + p->off_own);
     a.s = reinterpret_cast<float*>(w + p->off_s);
     a.omask = reinterpret_cast<uint32_t*>(w + p->off_omask);
+    a.pmask = reinterpret_cast<uint32_t*>(w + p->off_pmask);
     a.Q = reinterpret_cast<int8_t*>(w + p->off_q);
     return DPSGD_OK;
 }

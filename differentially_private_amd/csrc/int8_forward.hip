@@ -2,12 +2,12 @@
 // Cross-Record Precision Routing in Private Quantized Fine-Tuning", Sec. 4.2, Eq. 6 and
 // Algorithm 1; the LLM.int8 decomposition as its Sec. 2 describes it).
 //
-// Four launches per layer:
-//   k_i8_clear  zero the per-record outlier masks;
-//   k_i8_scan   per row: its owner record, the row scale s_i = max |a| over the entries below
-//               tau, and the per-entry test |a| >= tau OR-ed into the owner's mask (a segmented
-//               reduction by atomics; masks are bit sets of K bits per record);
-//   k_i8_quant  per row: codes round(127 a / s_i), zero in the owner's outlier columns;
+// Three launches per layer:
+//   k_i8_scan   per row: its owner record and the row scale s_i = max |a| over the entries below
+//               tau; per block of a record's rows: the OR of the per-entry tests |a| >= tau
+//               (the first level of a segmented reduction; masks are bit sets of K bits);
+//   k_i8_quant  per block: the record's outlier set O_r (OR of its blocks' masks), then the
+//               codes round(127 a / s_i) of the block's rows, zero in O_r's columns;
 //   k_i8_gemm   Y = fp16(dq16 + corr16): the exact integer product of the codes with the INT8
 //               weight on MFMA (v_mfma_i32_16x16x64_i8), dequantised in the epilogue, plus the
 //               FP16 correction of each row over its own record's outlier columns only.
@@ -66,86 +66,130 @@ __device__ __forceinline__ float wave_max(float v) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_i8_clear(uint32_t* p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        p[i] = 0u;
-}
+// Row blocks: record r owns max(1, ceil(len / 16)) blocks of up to 16 of its rows, numbered from
+// boff[r]; a workgroup takes one block, four rows per wavefront.
+constexpr int kScanRows = 16;
 
-// One wavefront per row (4 rows per workgroup).
-__global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.n) return;
-    // owner: the last record whose first row is <= row (empty records share a first row with
-    // the next one, so the last of them is the non-empty owner)
-    int64_t lo = 0, hi = a.n_rec - 1;
+struct RowBlock {
+    int64_t r, row0;
+    int nrows;
+};
+
+__device__ __forceinline__ bool row_block(const I8Args& a, RowBlock& rb) {
+    const int64_t* boff = a.offsets + a.n_rec + 1;
+    const int64_t blk = blockIdx.x;
+    if (blk >= boff[a.n_rec]) return false;
+    int64_t lo = 0, hi = a.n_rec - 1;        // the record whose blocks include blk
     while (lo < hi) {
         const int64_t mid = (lo + hi + 1) >> 1;
-        if (a.offsets[mid] <= row) lo = mid;
+        if (boff[mid] <= blk) lo = mid;
         else hi = mid - 1;
     }
-    if (lane == 0) a.own[row] = (int32_t)lo;
-    const uint16_t* x = a.A + row * a.K;
-    uint32_t* om = a.omask + lo * a.KW;
-    const bool on = a.tau_on != 0;
-    const float tau = a.tau;
-    float mx = 0.f;
-    if (a.a_vec) {
-        for (int64_t c = lane; c < a.K / 8; c += 64) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
-            uint32_t bits = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = fabsf(h2f(v[e >> 1] >> (16 * (e & 1))));
-                const bool o = on && f >= tau;
-                bits |= (uint32_t)o << e;
-                mx = o ? mx : fmaxf(mx, f);
-            }
-            if (bits) atomicOr(om + (8 * c) / 32, bits << ((8 * c) % 32));
-        }
-    } else {
-        for (int64_t j = lane; j < a.K; j += 64) {
-            const float f = fabsf(h2f(x[j]));
-            const bool o = on && f >= tau;
-            if (o) atomicOr(om + j / 32, 1u << (j % 32));
-            else mx = fmaxf(mx, f);
-        }
-    }
-    mx = wave_max(mx);
-    if (lane == 0) a.s[row] = mx;
+    rb.r = lo;
+    rb.row0 = a.offsets[lo] + kScanRows * (blk - boff[lo]);
+    const int64_t row_end = std::min<int64_t>(a.offsets[lo + 1], a.n);
+    rb.nrows = (int)std::max<int64_t>(0, std::min<int64_t>(kScanRows, row_end - rb.row0));
+    return true;
 }
 
-// One wavefront per row: codes of the row in Q (pitch Kp bytes, zero past K).
-__global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.n) return;
-    const uint16_t* x = a.A + row * a.K;
-    const uint32_t* om = a.omask + (int64_t)a.own[row] * a.KW;
-    const float s = a.s[row];
-    int8_t* q = a.Q + row * a.Kp;
-    if (a.a_vec) {
-        for (int64_t c = lane; c < a.Kp / 8; c += 64) {
-            uint32_t lo = 0, hi = 0;
-            if (8 * c < a.K) {
+// Per block: each row's owner and scale s_i = max |a| over the entries below tau, and the block's
+// partial outlier mask (the OR of its rows' per-entry tests |a| >= tau, taken in LDS) written
+// whole with plain stores, so nothing needs clearing between calls.
+__global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
+    __shared__ uint32_t wm[kI8MaxKW];
+    RowBlock rb;
+    if (!row_block(a, rb)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int KW = (int)a.KW;
+    for (int t = tid; t < KW; t += 256) wm[t] = 0u;
+    __syncthreads();
+    const bool on = a.tau_on != 0;
+    const float tau = a.tau;
+    for (int rr = w; rr < rb.nrows; rr += 4) {
+        const int64_t row = rb.row0 + rr;
+        const uint16_t* x = a.A + row * a.K;
+        float mx = 0.f;
+        if (a.a_vec) {
+            for (int64_t c = lane; c < a.K / 8; c += 64) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
-                const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+                uint32_t bits = 0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float f = h2f(v[e >> 1] >> (16 * (e & 1)));
-                    const int code = ((m >> e) & 1u) ? 0 : code_of(f, s);
-                    const uint32_t b = (uint32_t)(code & 0xFF) << (8 * (e & 3));
-                    if (e < 4) lo |= b;
-                    else hi |= b;
+                    const float f = fabsf(h2f(v[e >> 1] >> (16 * (e & 1))));
+                    const bool o = on && f >= tau;
+                    bits |= (uint32_t)o << e;
+                    mx = o ? mx : fmaxf(mx, f);
                 }
+                if (bits) atomicOr(wm + (8 * c) / 32, bits << ((8 * c) % 32));
             }
-            *reinterpret_cast<uint2*>(q + 8 * c) = make_uint2(lo, hi);
+        } else {
+            for (int64_t j = lane; j < a.K; j += 64) {
+                const float f = fabsf(h2f(x[j]));
+                if (on && f >= tau) atomicOr(wm + j / 32, 1u << (j % 32));
+                else mx = fmaxf(mx, f);
+            }
         }
-    } else {
-        for (int64_t j = lane; j < a.Kp; j += 64) {
-            int code = 0;
-            if (j < a.K && !((om[j / 32] >> (j % 32)) & 1u)) code = code_of(h2f(x[j]), s);
-            q[j] = (int8_t)code;
+        mx = wave_max(mx);
+        if (lane == 0) {
+            a.s[row] = mx;
+            a.own[row] = (int32_t)rb.r;
+        }
+    }
+    __syncthreads();
+    uint32_t* pm = a.pmask + (int64_t)blockIdx.x * KW;
+    for (int t = tid; t < KW; t += 256) pm[t] = wm[t];
+}
+
+// Per block: the record's outlier set O_r = OR of its blocks' partial masks (in LDS; the record's
+// first block also writes it out for the GEMM), then the codes of the block's rows in Q (pitch
+// Kp bytes, zero past K): round(127 a / s_i), zero in O_r's columns.
+__global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
+    __shared__ uint32_t om[kI8MaxKW];
+    RowBlock rb;
+    if (!row_block(a, rb)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int KW = (int)a.KW;
+    const int64_t* boff = a.offsets + a.n_rec + 1;
+    for (int t = tid; t < KW; t += 256) om[t] = 0u;
+    __syncthreads();
+    const int64_t b0 = boff[rb.r];
+    const int64_t pairs = (boff[rb.r + 1] - b0) * KW;
+    const uint32_t* pr = a.pmask + b0 * KW;
+    for (int64_t q = tid; q < pairs; q += 256) {
+        const uint32_t m = pr[q];
+        if (m) atomicOr(om + (int)(q % KW), m);
+    }
+    __syncthreads();
+    if ((int64_t)blockIdx.x == b0)
+        for (int t = tid; t < KW; t += 256) a.omask[rb.r * KW + t] = om[t];
+    for (int rr = w; rr < rb.nrows; rr += 4) {
+        const int64_t row = rb.row0 + rr;
+        const uint16_t* x = a.A + row * a.K;
+        const float s = a.s[row];
+        int8_t* q = a.Q + row * a.Kp;
+        if (a.a_vec) {
+            for (int64_t c = lane; c < a.Kp / 8; c += 64) {
+                uint32_t lo = 0, hi = 0;
+                if (8 * c < a.K) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
+                    const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = h2f(v[e >> 1] >> (16 * (e & 1)));
+                        const int code = ((m >> e) & 1u) ? 0 : code_of(f, s);
+                        const uint32_t b = (uint32_t)(code & 0xFF) << (8 * (e & 3));
+                        if (e < 4) lo |= b;
+                        else hi |= b;
+                    }
+                }
+                *reinterpret_cast<uint2*>(q + 8 * c) = make_uint2(lo, hi);
+            }
+        } else {
+            for (int64_t j = lane; j < a.Kp; j += 64) {
+                int code = 0;
+                if (j < a.K && !((om[j / 32] >> (j % 32)) & 1u)) code = code_of(h2f(x[j]), s);
+                q[j] = (int8_t)code;
+            }
         }
     }
 }
@@ -169,7 +213,7 @@ __global__ __launch_bounds__(256) void k_i8_weight(const uint16_t* __restrict__ 
 namespace {
 
 constexpr int kStages = 3;
-constexpr int kUC = 32;           // union columns staged per correction chunk
+constexpr int kUC = 16;           // union columns staged per correction chunk
 constexpr int kRS = kUC + 4;      // row stride (floats) of the staged residual
 
 // Byte offset of 16-byte chunk c (0..3) of row r inside a staged k-step (rows of 64 bytes):
@@ -185,6 +229,12 @@ __device__ __forceinline__ uint32_t stage_off(int r, int c) {
 // wavefronts of (16 FI) x (16 FO).  MFMA operand a = weight rows (o), b = code rows (i): lane l
 // of a 16x16 result holds row i = l % 16 and the four features 4 (l / 16) .. + 3, so the fp16
 // output is written 8 bytes per lane.
+//
+// The correction's operands (the tile's union of record outlier columns, each row's own bits,
+// the residual activations and the dequantised weight columns) are staged into their own LDS
+// region while the first k-steps' copies are in flight, so their gathers overlap the copy
+// latency instead of following the MFMA loop.  Unions wider than kUC columns are restaged chunk
+// by chunk after the loop.
 template <int FI, int FO, int WI, int WO>
 __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
     constexpr int NW = WI * WO, NT = 64 * NW;
@@ -192,9 +242,8 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
     constexpr int STAGE = (BI + BO) * 64;
     constexpr int CQ = BI / 16 / NW, CW = BO / 16 / NW;   // copies per wave per k-step
     static_assert(CQ * 16 * NW == BI && CW * 16 * NW == BO, "copy split");
-    constexpr int EPI = (BI + BI + BO + kI8MaxKW + kUC + 16) * 4 + (BI * kRS + kUC * BO) * 4;
-    constexpr int LDS = kStages * STAGE > EPI ? kStages * STAGE : EPI;
-    __shared__ __attribute__((aligned(16))) char lds[LDS];
+    constexpr int EPI = (BI + BI + BO + kI8MaxKW + kUC + 16 + BI) * 4 + (BI * kRS + kUC * BO) * 4;
+    __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE + EPI];
 
     const int64_t n = a.n, N = a.N;
     int ti, to;
@@ -237,50 +286,26 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
             copy16(pw, offw[q], dst + (uint32_t)(BI * 64 + (CW * w + q) * 1024));
     };
 
-    i32x4 acc[FO][FI];
-#pragma unroll
-    for (int f = 0; f < FO; ++f)
-#pragma unroll
-        for (int e = 0; e < FI; ++e) acc[f][e] = i32x4{0, 0, 0, 0};
-
     const int64_t total = a.Kp / 64;
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k)
         if (k < total) issue(k, k);
-    int st = 0, stn = kStages - 1;
-    for (int64_t s = 0; s < total; ++s) {
-        // this wave's copies of step s are done once at most the later issued steps are in
-        // flight; the barrier publishes all waves' copies and retires step s - 1's stage
-        wait_copies<CQ + CW>(std::min<int64_t>(s + kStages - 2, total - 1) - s);
-        __syncthreads();
-        if (s + kStages - 1 < total) issue(s + kStages - 1, stn);
-        const char* S = lds + st * STAGE;
-        i32x4 bq[FI];
-#pragma unroll
-        for (int e = 0; e < FI; ++e) bq[e] = *reinterpret_cast<const i32x4*>(S + rd_q + e * 1024);
-#pragma unroll
-        for (int f = 0; f < FO; ++f) {
-            const i32x4 aw = *reinterpret_cast<const i32x4*>(S + rd_w + f * 1024);
-#pragma unroll
-            for (int e = 0; e < FI; ++e)
-                acc[f][e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw, bq[e], acc[f][e], 0, 0, 0);
-        }
-        st = st == kStages - 1 ? 0 : st + 1;
-        stn = stn == kStages - 1 ? 0 : stn + 1;
-    }
-    __syncthreads();   // every wave is done with the stages: the epilogue reuses the LDS
 
-    int* own_t = reinterpret_cast<int*>(lds);          // owner record of each tile row (-1 past n)
+    // ---- correction operands, staged while those copies are in flight
+    char* E = lds + kStages * STAGE;
+    int* own_t = reinterpret_cast<int*>(E);            // owner record of each tile row (-1 past n)
     float* sat = reinterpret_cast<float*>(own_t + BI);  // fl(s_i / 127)
     float* sbt = sat + BI;                              // fl(s_W / 127)
     uint32_t* tmask = reinterpret_cast<uint32_t*>(sbt + BO);   // union of the rows' record sets
-    int* cols = reinterpret_cast<int*>(tmask + kI8MaxKW);      // columns of the current chunk
+    int* cols = reinterpret_cast<int*>(tmask + kI8MaxKW);      // columns of the staged chunk
     int* wsum = cols + kUC;                                    // scan scratch (NW + 1)
-    float* Rt = reinterpret_cast<float*>(wsum + 16);           // [BI][kRS] residual a or 0
+    uint32_t* rbits = reinterpret_cast<uint32_t*>(wsum + 16);  // per tile row: chunk bits
+    float* Rt = reinterpret_cast<float*>(rbits + BI);          // [BI][kRS] residual a or 0
     float* Wt = Rt + BI * kRS;                                 // [kUC][BO] dequantised weight
     for (int t = tid; t < BI; t += NT) {
         const int64_t r = i0 + t;
-        own_t[t] = r < n ? a.own[r] : -1;
+        const int32_t ow = r < n ? a.own[r] : -1;
+        own_t[t] = r < n ? (ow >= 0 && ow < a.n_rec ? ow : 0) : -1;
         sat[t] = r < n ? div_rn(a.s[r], 127.f) : 0.f;
     }
     for (int t = tid; t < BO; t += NT) {
@@ -288,8 +313,6 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
         sbt[t] = o < N ? div_rn(a.sW[o], 127.f) : 0.f;
     }
     __syncthreads();
-
-    // FP16 correction over the union of the tile's record sets, in chunks of kUC columns
     const int rows_valid = (int)std::min<int64_t>(BI, n - i0);
     const int r_lo = own_t[0], r_hi = own_t[rows_valid - 1];
     const int KW = (int)a.KW;
@@ -339,30 +362,88 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
                 ++rank;
             }
         }
+        for (int t = tid; t < BI; t += NT) rbits[t] = 0u;
         __syncthreads();
-        for (int t = tid; t < BI * kUC; t += NT) {
-            const int il = t / kUC, u = t % kUC;
-            float v = 0.f;
-            if (u < nuc && il < rows_valid) {
-                const int col = cols[u];
-                const int r = own_t[il];
-                if ((a.omask[(int64_t)r * KW + col / 32] >> (col % 32)) & 1u)
-                    v = h2f(a.A[(i0 + il) * a.K + col]);
-            }
-            Rt[il * kRS + u] = v;
+        // rbits[il] bit u: chunk column u is in the outlier set of tile row il's record
+        for (int t = tid; t < rows_valid * nuc; t += NT) {
+            const int il = t / nuc, u = t - il * nuc;
+            const int col = cols[u];
+            if ((a.omask[(int64_t)own_t[il] * KW + col / 32] >> (col % 32)) & 1u)
+                atomicOr(&rbits[il], 1u << u);
         }
-        for (int t = tid; t < kUC * BO; t += NT) {
-            const int u = t / BO, ol = t % BO;
-            float v = 0.f;
-            if (u < nuc && o0 + ol < N)
-                v = h2f(f2h_rounded((float)a.Wq[(o0 + ol) * a.Kp + cols[u]] * sbt[ol]));
-            Wt[u * BO + ol] = v;
+        __syncthreads();
+        // residual pairs (row, u < nuc) and weight pairs (u < nuc, feature): loads from clamped
+        // in-bounds addresses, masked afterwards, four per thread issued back to back
+        const int nr = BI * nuc;
+        for (int t0 = tid; t0 < nr; t0 += 4 * NT) {
+            float v[4];
+            int at[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int t = t0 + k * NT;
+                const bool ok = t < nr;
+                const int il = ok ? t / nuc : 0;
+                const int u = ok ? t - il * nuc : 0;
+                const bool live = ok && ((rbits[il] >> u) & 1u);
+                const uint16_t raw = a.A[(i0 + (live ? il : 0)) * a.K + (live ? cols[u] : 0)];
+                v[k] = live ? h2f(raw) : 0.f;
+                at[k] = ok ? il * kRS + u : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (at[k] >= 0) Rt[at[k]] = v[k];
+        }
+        const int nw = nuc * BO;
+        for (int t0 = tid; t0 < nw; t0 += 4 * NT) {
+            float v[4];
+            int at[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int t = t0 + k * NT;
+                const bool ok = t < nw;
+                const int u = ok ? t / BO : 0, ol = t % BO;
+                const int64_t o = std::min<int64_t>(o0 + ol, N - 1);
+                const int8_t raw = a.Wq[o * a.Kp + cols[u]];
+                v[k] = (ok && o0 + ol < N) ? h2f(f2h_rounded((float)raw * sbt[ol])) : 0.f;
+                at[k] = ok ? u * BO + ol : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (at[k] >= 0) Wt[at[k]] = v[k];
         }
         __syncthreads();
     };
     if (n_chunks == 1) stage(0);
 
-    // one 16-row group at a time: correction (fp32, ascending columns), then
+    // ---- main loop: the exact integer product
+    i32x4 acc[FO][FI];
+#pragma unroll
+    for (int f = 0; f < FO; ++f)
+#pragma unroll
+        for (int e = 0; e < FI; ++e) acc[f][e] = i32x4{0, 0, 0, 0};
+    int st = 0, stn = kStages - 1;
+    for (int64_t s = 0; s < total; ++s) {
+        // this wave's copies of step s are done once at most the later issued steps are in
+        // flight; the barrier publishes all waves' copies and retires step s - 1's stage
+        wait_copies<CQ + CW>(std::min<int64_t>(s + kStages - 2, total - 1) - s);
+        __syncthreads();
+        if (s + kStages - 1 < total) issue(s + kStages - 1, stn);
+        const char* S = lds + st * STAGE;
+        i32x4 bq[FI];
+#pragma unroll
+        for (int e = 0; e < FI; ++e) bq[e] = *reinterpret_cast<const i32x4*>(S + rd_q + e * 1024);
+#pragma unroll
+        for (int f = 0; f < FO; ++f) {
+            const i32x4 aw = *reinterpret_cast<const i32x4*>(S + rd_w + f * 1024);
+#pragma unroll
+            for (int e = 0; e < FI; ++e)
+                acc[f][e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw, bq[e], acc[f][e], 0, 0, 0);
+        }
+        st = st == kStages - 1 ? 0 : st + 1;
+        stn = stn == kStages - 1 ? 0 : stn + 1;
+    }
+
+    // ---- epilogue, one 16-row group at a time: correction (fp32, ascending columns), then
     // Y = fp16(dq16 + corr16) with dq16 = fp16(fl(fl(float(acc) * fl(s_i/127)) * fl(s_W/127)))
 #pragma unroll
     for (int e = 0; e < FI; ++e) {
@@ -432,15 +513,13 @@ int64_t i8_tiles(int64_t n, int64_t N, int big) {
     return ((n + b - 1) / b) * ((N + b - 1) / b);
 }
 
+int64_t i8_scan_blocks(int64_t n, int64_t n_rec) { return (n + kScanRows - 1) / kScanRows + n_rec; }
+
 hipError_t launch_i8_route(const I8Args& a, hipStream_t s) {
-    const int64_t words = a.n_rec * a.KW;
-    if (words > 0)
-        hipLaunchKernelGGL(k_i8_clear, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)),
-                           dim3(256), 0, s, a.omask, words);
-    if (a.n > 0) {
-        const unsigned g = (unsigned)((a.n + 3) / 4);
-        hipLaunchKernelGGL(k_i8_scan, dim3(g), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(k_i8_quant, dim3(g), dim3(256), 0, s, a);
+    if (a.n_rec > 0) {
+        const dim3 g((unsigned)i8_scan_blocks(a.n, a.n_rec));
+        hipLaunchKernelGGL(k_i8_scan, g, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_i8_quant, g, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -214,7 +214,9 @@ constexpr int kI8MaxKW = 1024;     // outlier-mask words per record: K <= 32768
 struct I8Args {
     const uint16_t* A;
     int64_t n, K, Kp, KW, n_rec;   // rows, columns, code pitch (K rounded up to 64), K / 32 words
-    const int64_t* offsets;        // [n_rec + 1] record row offsets
+    const int64_t* offsets;        // [n_rec + 1] record row offsets, then [n_rec + 1] scan
+                                   // block offsets (record r: max(1, ceil(len / 16)) blocks)
+    uint32_t* pmask;               // [scan blocks][KW] per-block partial outlier masks
     int32_t* own;                  // [n] owner record of each row
     float* s;                      // [n] row scales
     uint32_t* omask;               // [n_rec][KW] per-record outlier columns
@@ -229,6 +231,7 @@ struct I8Args {
     int32_t y_vec;                 // N % 4 == 0 and Y 8-byte aligned
 };
 int64_t i8_tiles(int64_t n, int64_t N, int big);
+int64_t i8_scan_blocks(int64_t n, int64_t n_rec);   // upper bound of sum max(1, ceil(len / 16))
 hipError_t launch_i8_route(const I8Args& a, hipStream_t s);
 hipError_t launch_i8_gemm(const I8Args& a, int big, hipStream_t s);
 hipError_t launch_i8_weight(const uint16_t* W, int64_t N, int64_t K, int64_t Kp, int8_t* Wq,

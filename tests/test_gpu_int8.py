@@ -213,3 +213,40 @@ def test_opt125m_layer_shapes(K, N):
     A, offsets, _, _ = gen.activations(K * 7 + N, [256] * 16, K)
     L = Layer(gen.weights(K + 3 * N, N, K))
     check(A, offsets, L)
+
+
+def test_graph_replay_matches_eager():
+    """Three layers' forwards captured into one HIP graph: every replay (with eager work and
+    synchronisations between replays) gives bitwise the eager outputs."""
+    lens = [64] * 4
+    shapes = [(256, 128), (128, 384), (384, 96)]
+    plan = dp.I8Plan(256, 4, 384)
+    ws = plan.workspace(DEV)
+    A_dev, layers, Ys = [], [], []
+    for idx, (K, N) in enumerate(shapes):
+        A, offsets, _, _ = gen.activations(40 + idx, lens, K, p_owned=1.0)
+        A_dev.append(torch.from_numpy(A).to(DEV))
+        layers.append(Layer(gen.weights(40 + idx, N, K)))
+        Ys.append(torch.empty((256, N), dtype=torch.float16, device=DEV))
+    dp.i8_set_records(plan, ws, offsets)
+
+    def fwd():
+        for A, L, Y in zip(A_dev, layers, Ys):
+            dp.i8_forward(plan, ws, 256, 4, A, A.shape[1], L.wq, L.sw, L.N, 6.0, Y)
+
+    fwd()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in Ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for rep in range(4):
+        for y in Ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(Ys, eager):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16)), rep
+        fwd()          # eager work between replays
+        torch.cuda.synchronize()
