@@ -468,26 +468,30 @@ def int8_line(args, torch, dev, dp):
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import int8_forward as o8      # host baseline only
-        per_shape = {}
-        t_start = time.perf_counter()
-        for K, N, count in ((768, 2304, 12), (768, 768, 12), (768, 3072, 12), (3072, 768, 12)):
+        shapes = []
+        for K, N in ((768, 2304), (768, 768), (768, 3072), (3072, 768)):
             L = next(x for x in m["layers"] if x["K"] == K and x["N"] == N)
-            A = L["A"].cpu().numpy()
             W = np.random.default_rng(K + N).standard_normal((N, K)).astype(np.float16)
             Wq, sW, _ = o8.quantize_weight(W)
-            t0 = time.perf_counter()
-            o8.forward(A, m["offsets"], Wq, sW, 6.0)
-            per_shape[(K, N)] = (time.perf_counter() - t0, count)
-        step_s = sum(t * c for t, c in per_shape.values())
+            shapes.append((L["A"].cpu().numpy(), Wq, sW))
+        t_start = time.perf_counter()
+        reps = 0
+        while True:     # whole passes over the four shapes (one block), at least cpu_seconds
+            for A, Wq, sW in shapes:
+                o8.forward(A, m["offsets"], Wq, sW, 6.0)
+            reps += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds:
+                break
+        step_s = 12 * (time.perf_counter() - t_start) / reps
         try:
             import threadpoolctl
             threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
         except Exception:
             threads = os.cpu_count()
         cpu = {"value": B / step_s, "unit": "records/s", "cores": threads, "kind": "oracle",
-               "sample": "one forward of each shape (qkv 768->2304, out 768->768, fc1 "
-                         "768->3072, fc2 3072->768) over the 16 x 256-token batch, times the 12 "
-                         "blocks "
+               "sample": f"{reps} passes over one block's four forwards (qkv 768->2304, out "
+                         "768->768, fc1 768->3072, fc2 3072->768) on the 16 x 256-token batch, "
+                         "times the 12 blocks "
                          f"({time.perf_counter() - t_start:.1f} s wall; numpy, BLAS threads)"}
 
     line = {"metric": "records/sec, record-owned LLM.int8 forward of a frozen backbone",
