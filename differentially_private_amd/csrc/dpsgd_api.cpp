@@ -13,6 +13,7 @@
 
 #include "../../include/dpsgd.h"
 #include "internal.h"
+#include "int8.h"
 
 using namespace dpsgd;
 

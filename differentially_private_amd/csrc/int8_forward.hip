@@ -27,6 +27,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "int8.h"
 
 namespace dpsgd {
 
