@@ -1077,7 +1077,7 @@ int dpsgd_i8_matmul(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n_
     if (int rc = i8_check_a(a, a_in, 6.0f)) return rc;
     if (int rc = i8_check_w(a, wq, w_scale, n_out, y)) return rc;
     i8_set_a(a, a_in, 6.0f);
-    hipError_t e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 256 ? 1 : 0, (hipStream_t)stream);
+    hipError_t e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 128 ? 1 : 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "int8 gemm launch");
     return DPSGD_OK;
 }
@@ -1093,7 +1093,7 @@ int dpsgd_i8_forward(const dpsgd_i8_plan* p, void* ws, int64_t n_rows, int64_t n
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_i8_route(a, s);
     if (e != hipSuccess) return hip_fail(e, "int8 routing launch");
-    e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 256 ? 1 : 0, s);
+    e = launch_i8_gemm(a, i8_tiles(n_rows, n_out, 1) >= 128 ? 1 : 0, s);
     if (e != hipSuccess) return hip_fail(e, "int8 gemm launch");
     return DPSGD_OK;
 }

@@ -93,6 +93,11 @@ __device__ __forceinline__ bool row_block(const I8Args& a, RowBlock& rb) {
     return true;
 }
 
+// Rows of a block per wavefront, and 16-byte chunks per row and lane loaded together: all of a
+// wavefront's loads for up to RPW rows x CPL chunks are issued before any is used.
+constexpr int RPW = kScanRows / 4;
+constexpr int CPL = 2;
+
 // Per block: each row's owner and scale s_i = max |a| over the entries below tau, and the block's
 // partial outlier mask (the OR of its rows' per-entry tests |a| >= tau, taken in LDS) written
 // whole with plain stores, so nothing needs clearing between calls.
@@ -102,38 +107,69 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
     if (!row_block(a, rb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int KW = (int)a.KW;
-    for (int t = tid; t < KW; t += 256) wm[t] = 0u;
-    __syncthreads();
     const bool on = a.tau_on != 0;
     const float tau = a.tau;
-    for (int rr = w; rr < rb.nrows; rr += 4) {
-        const int64_t row = rb.row0 + rr;
-        const uint16_t* x = a.A + row * a.K;
-        float mx = 0.f;
-        if (a.a_vec) {
-            for (int64_t c = lane; c < a.K / 8; c += 64) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
-                uint32_t bits = 0;
+    float mx[RPW];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = fabsf(h2f(v[e >> 1] >> (16 * (e & 1))));
-                    const bool o = on && f >= tau;
-                    bits |= (uint32_t)o << e;
-                    mx = o ? mx : fmaxf(mx, f);
-                }
-                if (bits) atomicOr(wm + (8 * c) / 32, bits << ((8 * c) % 32));
+    for (int j = 0; j < RPW; ++j) mx[j] = 0.f;
+    // a record without rows has one block with no rows (row0 may be n): no loads at all then;
+    // otherwise masked-off loads read the block's first row, which exists
+    const bool vec = rb.nrows > 0 && a.a_vec;
+    const int64_t nch = a.K / 8;
+    u32x4 v[RPW][CPL];
+    auto load = [&](int64_t c0) {
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+            for (int b = 0; b < CPL; ++b) {
+                const int rr = w + 4 * j;
+                const int64_t c = c0 + 64 * b;
+                const bool ok = rr < rb.nrows && c < nch;
+                const uint16_t* x = a.A + (rb.row0 + (ok ? rr : 0)) * a.K + 8 * (ok ? c : 0);
+                v[j][b] = ok ? *reinterpret_cast<const u32x4*>(x) : u32x4{0u, 0u, 0u, 0u};
             }
-        } else {
-            for (int64_t j = lane; j < a.K; j += 64) {
-                const float f = fabsf(h2f(x[j]));
-                if (on && f >= tau) atomicOr(wm + j / 32, 1u << (j % 32));
-                else mx = fmaxf(mx, f);
+    };
+    if (vec) load(lane);
+    for (int t = tid; t < KW; t += 256) wm[t] = 0u;
+    __syncthreads();
+    if (vec) {
+        for (int64_t c0 = lane; c0 < nch; c0 += 64 * CPL) {
+            if (c0 != lane) load(c0);
+#pragma unroll
+            for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                for (int b = 0; b < CPL; ++b) {
+                    const int64_t c = c0 + 64 * b;
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = fabsf(h2f(v[j][b][e >> 1] >> (16 * (e & 1))));
+                        const bool o = on && f >= tau;
+                        bits |= (uint32_t)o << e;
+                        mx[j] = o ? mx[j] : fmaxf(mx[j], f);
+                    }
+                    if (bits) atomicOr(wm + (8 * c) / 32, bits << ((8 * c) % 32));
+                }
+        }
+    } else {
+        for (int j = 0; j < RPW; ++j) {
+            const int rr = w + 4 * j;
+            if (rr >= rb.nrows) break;
+            const uint16_t* x = a.A + (rb.row0 + rr) * a.K;
+            for (int64_t k = lane; k < a.K; k += 64) {
+                const float f = fabsf(h2f(x[k]));
+                if (on && f >= tau) atomicOr(wm + k / 32, 1u << (k % 32));
+                else mx[j] = fmaxf(mx[j], f);
             }
         }
-        mx = wave_max(mx);
-        if (lane == 0) {
-            a.s[row] = mx;
-            a.own[row] = (int32_t)rb.r;
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int rr = w + 4 * j;
+        const float m = wave_max(mx[j]);
+        if (lane == 0 && rr < rb.nrows) {
+            a.s[rb.row0 + rr] = m;
+            a.own[rb.row0 + rr] = (int32_t)rb.r;
         }
     }
     __syncthreads();
@@ -151,6 +187,30 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int KW = (int)a.KW;
     const int64_t* boff = a.offsets + a.n_rec + 1;
+    float sj[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int rr = w + 4 * j;
+        sj[j] = rr < rb.nrows ? a.s[rb.row0 + rr] : 0.f;
+    }
+    const bool vec = rb.nrows > 0 && a.a_vec;
+    const int64_t nch = a.K / 8, npc = a.Kp / 8;
+    // the block's activations for (up to) RPW rows x CPL chunks per lane, loaded before the mask
+    // reduction so that the two latencies overlap; a block without rows loads nothing
+    u32x4 v[RPW][CPL];
+    auto load = [&](int64_t c0) {
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+            for (int b = 0; b < CPL; ++b) {
+                const int rr = w + 4 * j;
+                const int64_t c = c0 + 64 * b;
+                const bool ok = rr < rb.nrows && c < nch;
+                const uint16_t* x = a.A + (rb.row0 + (ok ? rr : 0)) * a.K + 8 * (ok ? c : 0);
+                v[j][b] = ok ? *reinterpret_cast<const u32x4*>(x) : u32x4{0u, 0u, 0u, 0u};
+            }
+    };
+    if (vec) load(lane);
     for (int t = tid; t < KW; t += 256) om[t] = 0u;
     __syncthreads();
     const int64_t b0 = boff[rb.r];
@@ -163,33 +223,42 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
     __syncthreads();
     if ((int64_t)blockIdx.x == b0)
         for (int t = tid; t < KW; t += 256) a.omask[rb.r * KW + t] = om[t];
-    for (int rr = w; rr < rb.nrows; rr += 4) {
-        const int64_t row = rb.row0 + rr;
-        const uint16_t* x = a.A + row * a.K;
-        const float s = a.s[row];
-        int8_t* q = a.Q + row * a.Kp;
-        if (a.a_vec) {
-            for (int64_t c = lane; c < a.Kp / 8; c += 64) {
-                uint32_t lo = 0, hi = 0;
-                if (8 * c < a.K) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * c);
-                    const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+    if (vec) {
+        for (int64_t c0 = lane; c0 < npc; c0 += 64 * CPL) {
+            if (c0 != lane) load(c0);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float f = h2f(v[e >> 1] >> (16 * (e & 1)));
-                        const int code = ((m >> e) & 1u) ? 0 : code_of(f, s);
-                        const uint32_t b = (uint32_t)(code & 0xFF) << (8 * (e & 3));
-                        if (e < 4) lo |= b;
-                        else hi |= b;
+            for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                for (int b = 0; b < CPL; ++b) {
+                    const int rr = w + 4 * j;
+                    const int64_t c = c0 + 64 * b;
+                    if (rr >= rb.nrows || c >= npc) continue;
+                    uint32_t lo = 0, hi = 0;
+                    if (c < nch) {
+                        const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float f = h2f(v[j][b][e >> 1] >> (16 * (e & 1)));
+                            const int code = ((m >> e) & 1u) ? 0 : code_of(f, sj[j]);
+                            const uint32_t bb = (uint32_t)(code & 0xFF) << (8 * (e & 3));
+                            if (e < 4) lo |= bb;
+                            else hi |= bb;
+                        }
                     }
+                    *reinterpret_cast<uint2*>(a.Q + (rb.row0 + rr) * a.Kp + 8 * c) = make_uint2(lo, hi);
                 }
-                *reinterpret_cast<uint2*>(q + 8 * c) = make_uint2(lo, hi);
-            }
-        } else {
-            for (int64_t j = lane; j < a.Kp; j += 64) {
+        }
+    } else {
+        for (int j = 0; j < RPW; ++j) {
+            const int rr = w + 4 * j;
+            if (rr >= rb.nrows) break;
+            const int64_t row = rb.row0 + rr;
+            const uint16_t* x = a.A + row * a.K;
+            int8_t* q = a.Q + row * a.Kp;
+            for (int64_t k = lane; k < a.Kp; k += 64) {
                 int code = 0;
-                if (j < a.K && !((om[j / 32] >> (j % 32)) & 1u)) code = code_of(h2f(x[j]), s);
-                q[j] = (int8_t)code;
+                if (k < a.K && !((om[k / 32] >> (k % 32)) & 1u)) code = code_of(h2f(x[k]), sj[j]);
+                q[k] = (int8_t)code;
             }
         }
     }
