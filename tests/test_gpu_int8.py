@@ -250,3 +250,50 @@ def test_graph_replay_matches_eager():
             assert torch.equal(y.view(torch.int16), e.view(torch.int16)), rep
         fwd()          # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_wide_layer_and_odd_features():
+    """k = 16384 (512 mask words per record, tile unions over many words), 203 output features
+    (no 8-byte output stores), records of 100-300 rows."""
+    say("int8 wide layer")
+    A, offsets, _, _ = gen.activations(61, [100, 300, 160], 16384, n_shared=5, p_owned=1.0)
+    L = Layer(gen.weights(61, 203, 16384))
+    check(A, offsets, L)
+
+
+def test_misaligned_activations():
+    """Activation rows whose base is 2 bytes past a 16-byte boundary take the element-wise load
+    path even with k a multiple of 8; same results as the aligned buffer."""
+    A, offsets, _, _ = gen.activations(62, [40, 25], 64, p_owned=1.0)
+    L = Layer(gen.weights(62, 36, 64))
+    n, K = A.shape
+    plan = dp.I8Plan(n, 2, K)
+    ws = plan.workspace(DEV)
+    buf = torch.zeros(n * K + 8, dtype=torch.float16, device=DEV)
+    buf[1:1 + n * K] = torch.from_numpy(A.reshape(-1)).to(DEV)
+    mis = buf[1:1 + n * K]
+    assert mis.data_ptr() % 16 != 0
+    Y = torch.empty((n, L.N), dtype=torch.float16, device=DEV)
+    dp.i8_set_records(plan, ws, offsets)
+    dp.i8_forward(plan, ws, n, 2, mis, K, L.wq, L.sw, L.N, 6.0, Y)
+    torch.cuda.synchronize()
+    ref = o8.forward(A, offsets, L.Wq_ref, L.sW_ref, 6.0)
+    assert np.array_equal(Y.cpu().numpy().view(np.uint16), ref["Y"].view(np.uint16))
+
+
+def test_thousand_short_records():
+    """1,000 records of 0-5 rows: the owner search over many records, tiles spanning hundreds of
+    records (and empty ones between them)."""
+    rng = np.random.default_rng(63)
+    lens = rng.integers(0, 6, 1000)
+    A, offsets, _, _ = gen.activations(63, lens, 96, p_owned=0.5)
+    L = Layer(gen.weights(63, 72, 96))
+    check(A, offsets, L)
+
+
+def test_max_width():
+    """The largest supported k (32768): mask words at the limit of a tile's union buffer."""
+    say("int8 max width")
+    A, offsets, _, _ = gen.activations(64, [20, 12], 32768, n_shared=8, p_owned=1.0)
+    L = Layer(gen.weights(64, 40, 32768))
+    check(A, offsets, L)
