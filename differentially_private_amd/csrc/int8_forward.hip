@@ -442,9 +442,12 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
                 atomicOr(&rbits[il], 1u << u);
         }
         __syncthreads();
-        // residual pairs (row, u < nuc) and weight pairs (u < nuc, feature): loads from clamped
-        // in-bounds addresses, masked afterwards, four per thread issued back to back
-        const int nr = BI * nuc;
+        // residual pairs (row, u) and weight pairs (u, feature) for u < nuc4 (nuc rounded up to 4;
+        // the padding is zero on both sides, so the correction loop runs in whole groups of four
+        // and a zero product leaves the fp32 sum unchanged): loads from clamped in-bounds addresses,
+        // masked afterwards, four per thread issued back to back
+        const int nuc4 = (nuc + 3) & ~3;
+        const int nr = BI * nuc4;
         for (int t0 = tid; t0 < nr; t0 += 4 * NT) {
             float v[4];
             int at[4];
@@ -452,9 +455,9 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
             for (int k = 0; k < 4; ++k) {
                 const int t = t0 + k * NT;
                 const bool ok = t < nr;
-                const int il = ok ? t / nuc : 0;
-                const int u = ok ? t - il * nuc : 0;
-                const bool live = ok && ((rbits[il] >> u) & 1u);
+                const int il = ok ? t / nuc4 : 0;
+                const int u = ok ? t - il * nuc4 : 0;
+                const bool live = ok && u < nuc && ((rbits[il] >> u) & 1u);
                 const uint16_t raw = a.A[(i0 + (live ? il : 0)) * a.K + (live ? cols[u] : 0)];
                 v[k] = live ? h2f(raw) : 0.f;
                 at[k] = ok ? il * kRS + u : -1;
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
             for (int k = 0; k < 4; ++k)
                 if (at[k] >= 0) Rt[at[k]] = v[k];
         }
-        const int nw = nuc * BO;
+        const int nw = nuc4 * BO;
         for (int t0 = tid; t0 < nw; t0 += 4 * NT) {
             float v[4];
             int at[4];
@@ -472,9 +475,10 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
                 const int t = t0 + k * NT;
                 const bool ok = t < nw;
                 const int u = ok ? t / BO : 0, ol = t % BO;
+                const bool live = ok && u < nuc && o0 + ol < N;
                 const int64_t o = std::min<int64_t>(o0 + ol, N - 1);
-                const int8_t raw = a.Wq[o * a.Kp + cols[u]];
-                v[k] = (ok && o0 + ol < N) ? h2f(f2h_rounded((float)raw * sbt[ol])) : 0.f;
+                const int8_t raw = a.Wq[o * a.Kp + (live ? cols[u] : 0)];
+                v[k] = live ? h2f(f2h_rounded((float)raw * sbt[ol])) : 0.f;
                 at[k] = ok ? u * BO + ol : -1;
             }
 #pragma unroll
@@ -515,6 +519,10 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
 
     // ---- epilogue, one 16-row group at a time: correction (fp32, ascending columns), then
     // Y = fp16(dq16 + corr16) with dq16 = fp16(fl(fl(float(acc) * fl(s_i/127)) * fl(s_W/127)))
+    f4 sbv[FO];   // fl(s_W/127) of the lane's four features in each 16-feature block
+#pragma unroll
+    for (int f = 0; f < FO; ++f) sbv[f] = *reinterpret_cast<const f4*>(sbt + 16 * FO * wo + 16 * f + 4 * g);
+    const bool interior = a.y_vec && i0 + BI <= n && o0 + BO <= N;   // uniform per workgroup
 #pragma unroll
     for (int e = 0; e < FI; ++e) {
         const int il = 16 * FI * wi + 16 * e + l16;
@@ -523,13 +531,12 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
         for (int f = 0; f < FO; ++f) corr[f] = f4{0.f, 0.f, 0.f, 0.f};
         for (int ch = 0; ch < n_chunks; ++ch) {
             if (n_chunks > 1) stage(ch * kUC);
-            const int nuc = std::min(kUC, nu - ch * kUC);
+            const int nuc4 = (std::min(kUC, nu - ch * kUC) + 3) & ~3;
             const float* rrow = Rt + il * kRS;
-            for (int u = 0; u < nuc; u += 4) {
+            for (int u = 0; u < nuc4; u += 4) {
                 const f4 rv = *reinterpret_cast<const f4*>(rrow + u);
 #pragma unroll
-                for (int uu = 0; uu < 4; ++uu) {
-                    if (u + uu >= nuc) break;
+                for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
                     for (int f = 0; f < FO; ++f) {
                         const f4 wv = *reinterpret_cast<const f4*>(
@@ -537,31 +544,33 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) corr[f][r] = fmaf(rv[uu], wv[r], corr[f][r]);
                     }
-                }
             }
         }
         const int64_t i = i0 + il;
         const float sa = sat[il];
 #pragma unroll
         for (int f = 0; f < FO; ++f) {
-            const int obl = 16 * FO * wo + 16 * f + 4 * g;
-            const int64_t ob = o0 + obl;
+            const int64_t ob = o0 + 16 * FO * wo + 16 * f + 4 * g;
             uint16_t y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float d = h2f(f2h_rounded(((float)acc[f][e][r] * sa) * sbt[obl + r]));
+                const float d = h2f(f2h_rounded(((float)acc[f][e][r] * sa) * sbv[f][r]));
                 const float c = h2f(f2h_rounded(corr[f][r]));
                 y[r] = f2h(d + c);
             }
-            if (i >= n) continue;
             uint16_t* dst = a.Y + i * N + ob;
-            if (a.y_vec && ob + 4 <= N) {
-                *reinterpret_cast<uint2*>(dst) =
-                    make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
-            } else {
+            const uint2 packed = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16),
+                                            (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+            if (interior) {
+                *reinterpret_cast<uint2*>(dst) = packed;
+            } else if (i < n) {
+                if (a.y_vec && ob + 4 <= N) {
+                    *reinterpret_cast<uint2*>(dst) = packed;
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (ob + r < N) dst[r] = y[r];
+                    for (int r = 0; r < 4; ++r)
+                        if (ob + r < N) dst[r] = y[r];
+                }
             }
         }
     }
