@@ -465,6 +465,41 @@ def int8_line(args, torch, dev, dp):
             "kernel": "k_i8_gemm (INT8 MFMA, dequantisation + record-owned FP16 correction)",
             "algorithmic_ops_per_launch": ops / launches, "avg_ms": avg_ms, "launches": launches}
 
+    # the same kernels on one 7B-shaped frozen projection (4096 -> 4096) over 16 records x 512
+    # tokens, where the INT8 product is large enough for the GEMM's MFMA efficiency to show
+    from datagen import int8 as gen
+    lens7, K7, N7 = [512] * 16, 4096, 4096
+    A7, off7, _, _ = gen.activations(77, lens7, K7)
+    n7 = int(off7[-1])
+    dA7 = torch.from_numpy(A7).to(dev)
+    W7 = torch.from_numpy(gen.weights(77, N7, K7)).to(dev)
+    wq7 = torch.empty((N7, dp.i8_pitch(K7)), dtype=torch.int8, device=dev)
+    sw7 = torch.empty(N7, dtype=torch.float32, device=dev)
+    dp.i8_quantize_weight(W7, N7, K7, wq7, sw7)
+    Y7 = torch.empty((n7, N7), dtype=torch.float16, device=dev)
+    plan7 = dp.I8Plan(n7, len(lens7), K7)
+    ws7 = plan7.workspace(dev)
+    dp.i8_set_records(plan7, ws7, off7, stream)
+    for _ in range(3):
+        dp.i8_forward(plan7, ws7, n7, len(lens7), dA7, K7, wq7, sw7, N7, 6.0, Y7, stream)
+    g7_ms, f7_ms = 0.0, 0.0
+    reps7 = max(3, args.steps // 5)
+    for _ in range(reps7):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        dp.i8_route(plan7, ws7, n7, len(lens7), dA7, K7, 6.0, stream)
+        e1.record(stream)
+        dp.i8_matmul(plan7, ws7, n7, len(lens7), dA7, K7, wq7, sw7, N7, Y7, stream)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        f7_ms += e0.elapsed_time(e2)
+        g7_ms += e1.elapsed_time(e2)
+    ops7 = 2 * n7 * K7 * N7
+    large = {"shape": f"{n7} x {K7} -> {N7} (16 records x 512 tokens)", "forward_ms": f7_ms / reps7,
+             "gemm_ms": g7_ms / reps7, "gemm_TOPs": ops7 / (g7_ms / reps7 * 1e-3) / 1e12,
+             "gemm_frac": ops7 / (g7_ms / reps7 * 1e-3) / 1e12 / I8_PEAK_TOPS}
+    del dA7, W7, wq7, Y7, ws7
+
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import int8_forward as o8      # host baseline only
@@ -504,7 +539,7 @@ def int8_line(args, torch, dev, dp):
                        "records": B, "tokens": m["T"], "rows": n, "tau": 6.0,
                        "timing": "HIP graph of the 48 forwards; record offsets set before"},
             "roofline": roof, "cpu_baseline": cpu,
-            "eager_ms_per_step": eager_ms,
+            "eager_ms_per_step": eager_ms, "large_layer": large,
             "batched_union": {"graph_ms_per_step": batched_graph_ms,
                               "eager_ms_per_step": batched_eager_ms},
             "tokens_per_s": n / (graph_ms * 1e-3)}
