@@ -268,11 +268,21 @@ def secondary(args, w, torch, dev, dp, datagen):
             x1.record(stream)
             torch.cuda.synchronize()
             return x0.elapsed_time(x1) / args.steps
-        # each phase alone on physical batch 0 (K back-to-back calls between HIP events)
-        phase["norms"] = timed(lambda: dp.norms(plan, w.B, 0, L, As, Gs, ws)) * w.n_phys
-        phase["clip"] = timed(lambda: dp.clip(plan, w.B, w.C, ws)) * w.n_phys
-        phase["clipped_sum"] = timed(
-            lambda: dp.clipped_sum(plan, w.B, 0, L, As, Gs, None, out, ws)) * w.n_phys
+        # each phase alone on physical batch 0 (K back-to-back calls between HIP events), with
+        # the C calls' arguments marshalled once so that the host does not pace the GPU
+        lib = dp.load()
+        arr_a, arr_g, arr_o = dp._ptr_array(As), dp._ptr_array(Gs), dp._ptr_array(out)
+        wsp, sp = ws.data_ptr(), stream.cuda_stream
+
+        def checked(rc):
+            if rc:
+                dp._check(rc)
+        phase["norms"] = timed(lambda: checked(lib.dpsgd_norms(plan.handle, w.B, 0, L, arr_a, arr_g,
+                                                               wsp, sp))) * w.n_phys
+        phase["clip"] = timed(lambda: checked(lib.dpsgd_clip(plan.handle, w.B, w.C, 0, wsp, None,
+                                                             None, sp))) * w.n_phys
+        phase["clipped_sum"] = timed(lambda: checked(lib.dpsgd_clipped_sum(
+            plan.handle, w.B, 0, L, arr_a, arr_g, None, arr_o, 0, wsp, sp))) * w.n_phys
         phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws,
                                                 params=theta, lr=DESCENT_LR, normalizer=DESCENT_L))
         phase["rest_of_step"] = ms - phase["norms"]   # residual: the step minus the norms timed alone
