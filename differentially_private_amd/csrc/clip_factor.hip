@@ -22,20 +22,17 @@ __global__ __launch_bounds__(1024) void k_clip(ClipArgs a) {
     for (int64_t rec0 = w; rec0 < a.n_rec; rec0 += 4 * nw) {
         double s4[4];
         record_norm2_x4(a.parts, a.parts_stride, a.n_parts, rec0, nw, a.n_rec, lane, s4);
-        if (lane == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t rec = rec0 + j * nw;
-                if (rec >= a.n_rec) break;
-                const double s = s4[j];
-                const double n = sqrt(s);
-                const double cf = (n <= a.C) ? 1.0 : a.C / n;
-                if (!isfinite(s)) atomicOr(&bad, 1u);
-                a.n_ws[rec] = (float)n;
-                a.c_ws[rec] = (float)cf;
-                if (a.n_user) a.n_user[rec] = (float)n;
-                if (a.c_user) a.c_user[rec] = (float)cf;
-            }
+        // every lane holds the four sums; lane j < 4 finishes record rec0 + j nw
+        const int64_t rec = rec0 + (int64_t)lane * nw;
+        if (lane < 4 && rec < a.n_rec) {
+            const double s = lane == 0 ? s4[0] : lane == 1 ? s4[1] : lane == 2 ? s4[2] : s4[3];
+            const double n = sqrt(s);
+            const double cf = (n <= a.C) ? 1.0 : a.C / n;
+            if (!isfinite(s)) atomicOr(&bad, 1u);
+            a.n_ws[rec] = (float)n;
+            a.c_ws[rec] = (float)cf;
+            if (a.n_user) a.n_user[rec] = (float)n;
+            if (a.c_user) a.c_user[rec] = (float)cf;
         }
     }
     __syncthreads();

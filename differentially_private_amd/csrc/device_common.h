@@ -30,22 +30,38 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// v from lane (lane ^ k) for the patterns one DPP move reaches inside a row of 16
+// lanes (CTRL: 0xB1 quad_perm 1,0,3,2 = k 1; 0x4E quad_perm 2,3,0,1 = k 2; 0x1B
+// quad_perm 3,2,1,0 = k 3; 0x141 row_half_mirror = k 7; 0x128 row_ror 8 = k 8).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The same butterfly as wave_sum (partner lane ^ 32, ^ 16, ..., ^ 1, each step
+// v + partner) in fp64; the steps inside a row of 16 lanes move the partner's value
+// with DPP instead of an LDS permute.  The moves are exact, so the result is the one
+// the all-shuffle butterfly gives.
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += __shfl_xor(v, 32, 64);
+    v += __shfl_xor(v, 16, 64);
+    v += dpp_d<0x128>(v);                // lane ^ 8
+    v += dpp_d<0x141>(dpp_d<0x1B>(v));   // lane ^ 4 = (lane ^ 3) ^ 7
+    v += dpp_d<0x4E>(v);                 // lane ^ 2
+    v += dpp_d<0xB1>(v);                 // lane ^ 1
     return v;
 }
 
-// Squared norms of up to four records from their partials (record r's partials
-// at parts + r * stride, n_parts of them): every lane sums partials lane,
-// lane + 64, ... in ascending order in fp64 (a partial past the end adds +0,
-// which changes no sum of squares), then a fixed butterfly combines the lanes.  The per-record order depends only on n_parts, never on which or how
-// many records are reduced together, so every caller gets bitwise the same
-// value for a record.  Records >= n_rec are skipped (their result is 0).
-__device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts, int64_t stride,
-                                                int64_t n_parts, int64_t rec0, int64_t rec_step,
-                                                int64_t n_rec, int lane, double (&out)[4]) {
-    double s[4] = {0.0, 0.0, 0.0, 0.0};
+// One batch of partials for up to four records (record rec0 + j * rec_step holds its
+// partials at parts + rec * stride, n_parts of them): lane values k0, k0 + 64, ...,
+// k0 + 448.  A partial past the end, or a record >= n_rec, reads an in-bounds
+// address and yields +0, so the loads are unconditional and issue back to back.
+__device__ __forceinline__ void record_parts_load_x4(const float* __restrict__ parts, int64_t stride,
+                                                     int64_t n_parts, int64_t rec0, int64_t rec_step,
+                                                     int64_t n_rec, int64_t k0, float (&v)[4][8]) {
     const float* p[4];
     bool ok[4];
 #pragma unroll
@@ -54,18 +70,34 @@ __device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts,
         ok[j] = rec < n_rec;
         p[j] = parts + (ok[j] ? rec : 0) * stride;
     }
-    // batches of 8 partials per lane and record: 32 independent loads in flight.  Every
-    // load reads an in-bounds address (clamped) and the value is masked afterwards, so the
-    // loads are unconditional and issue back to back.
-    for (int64_t k0 = lane; k0 < n_parts; k0 += 64 * 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t k = k0 + 64 * u;
+        const int64_t kc = k < n_parts ? k : n_parts - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j][u] = keep_or_zero(p[j][kc], ok[j] && k < n_parts);
+    }
+}
+
+// Squared norms of up to four records from their partials, the first batch (k0 =
+// lane) already loaded into v0 by record_parts_load_x4: every lane sums its
+// partials lane, lane + 64, ... in ascending order in fp64 (the +0 of a partial
+// past the end changes no sum of squares), then a fixed butterfly combines the
+// lanes.  The per-record order depends only on n_parts, never on which or how many
+// records are reduced together, so every caller gets bitwise the same value for a
+// record.  Records >= n_rec are skipped (their result is 0).
+__device__ __forceinline__ void record_norm2_x4_from(const float (&v0)[4][8],
+                                                     const float* __restrict__ parts, int64_t stride,
+                                                     int64_t n_parts, int64_t rec0, int64_t rec_step,
+                                                     int64_t n_rec, int lane, double (&out)[4]) {
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[j] += (double)v0[j][u];
+    for (int64_t k0 = lane + 64 * 8; k0 < n_parts; k0 += 64 * 8) {
         float v[4][8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t k = k0 + 64 * u;
-            const int64_t kc = k < n_parts ? k : n_parts - 1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j][u] = keep_or_zero(p[j][kc], ok[j] && k < n_parts);
-        }
+        record_parts_load_x4(parts, stride, n_parts, rec0, rec_step, n_rec, k0, v);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -73,6 +105,14 @@ __device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts,
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = wave_sum_d(s[j]);
+}
+
+__device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts, int64_t stride,
+                                                int64_t n_parts, int64_t rec0, int64_t rec_step,
+                                                int64_t n_rec, int lane, double (&out)[4]) {
+    float v0[4][8];
+    record_parts_load_x4(parts, stride, n_parts, rec0, rec_step, n_rec, lane, v0);
+    record_norm2_x4_from(v0, parts, stride, n_parts, rec0, rec_step, n_rec, lane, out);
 }
 
 // LDS byte address of a pointer into a __shared__ array

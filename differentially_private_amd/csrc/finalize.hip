@@ -12,71 +12,89 @@
 // publishes n_i, c_i and the status word.  Otherwise the factors come from a
 // preceding clip_factor launch.  A nonfinite norm skips every write to out.
 #include <algorithm>
+#include <atomic>
 
 #include "philox.h"
 
 namespace dpsgd {
 
 constexpr int kFinalBatch = 16;  // records whose blocks a thread loads before the clip prologue
+constexpr int kFinalMaxThreads = 512;
 
-// Grid: x = 256-thread chunks of a layer (4 elements per thread), y = layer of the
-// launch.  Element x of layer l has flat index off_l + x.
-template <bool CLIP_INSIDE>
-__global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
+// Grid: x = chunks of a layer (4 elements per thread, 64 * nw threads, nw chosen by
+// the host so that the grid is about one workgroup per compute unit), y = layer of
+// the launch.  Element x of layer l has flat index off_l + x.  VEC: every layer of the
+// launch has n_l and off_l multiples of 4 and 16-byte aligned blocks (checked on the
+// host), so the gradient loads are unconditional 16-byte loads (a thread past the end
+// of its layer loads the layer's last four elements and stores nothing).  Loads
+// complete in issue order and the compiler counts them exactly only when no branch
+// decides whether they are issued, so this is what lets the clip prologue wait for
+// its own loads alone while the gradient blocks are still in flight.
+template <bool CLIP_INSIDE, bool VEC>
+__global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
     __shared__ float cs[kFinalMaxRecords];
     __shared__ uint32_t bad;
     const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int nw = (int)(blockDim.x >> 6);
     const int l = blockIdx.y;
     const int64_t off = a.off[l];
     const int64_t n_l = a.off[l + 1] - off;
     const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + tid) * 4;
     const bool active = x0 < n_l;
     float* th = a.params[l];   // descent step target, or null
-    const bool vec = active && x0 + 4 <= n_l && (n_l & 3) == 0 && (off & 3) == 0 &&
-                     ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.src[l]) |
-                       reinterpret_cast<uintptr_t>(th)) & 15u) == 0;
-    const float* src = a.src[l] + x0;
+    const bool vec = VEC ? active
+                         : active && x0 + 4 <= n_l && (n_l & 3) == 0 && (off & 3) == 0 &&
+                               ((reinterpret_cast<uintptr_t>(a.out[l]) |
+                                 reinterpret_cast<uintptr_t>(a.src[l]) |
+                                 reinterpret_cast<uintptr_t>(th)) & 15u) == 0;
 
-    // 1) the first batch of this thread's gradient-block loads, independent of the factors
+    // 1) what the clip factors depend on, issued first: the status word and the first
+    //    batch of partials of this wave's first four records (w, w + nw, w + 2 nw, w + 3 nw)
+    const uint32_t status0 = *a.status;
+    float pv[4][8];
+    if (CLIP_INSIDE) record_parts_load_x4(a.parts, a.parts_stride, a.n_parts, w, nw, a.n_rec, lane, pv);
+
+    // 2) the first batch of this thread's gradient-block loads, independent of the factors
+    const float* src = a.src[l] + (VEC && !active ? n_l - 4 : x0);
     f32x4 v[kFinalBatch];
     const int64_t nb0 = a.n_rec < kFinalBatch ? a.n_rec : kFinalBatch;
-    if (vec) {
+    if (VEC || vec) {
 #pragma unroll
         for (int u = 0; u < kFinalBatch; ++u)   // unconditional: rows past n_rec repeat the last
             v[u] = *reinterpret_cast<const f32x4*>(src + (u < nb0 ? u : nb0 - 1) * n_l);
     }
 
-    // 2) this thread's normals (Philox + Box-Muller), computed while the loads are in flight
+    // 3) this thread's normals (Philox + Box-Muller), computed while the loads are in flight
     float z[4] = {0.f, 0.f, 0.f, 0.f};
     if (a.noise && vec) gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
 
-    // 3) clip factors
+    // 4) clip factors
     const float* cf = a.clip;
     bool skip;
     if (CLIP_INSIDE) {
-        const uint32_t old = a.accumulate ? *a.status : 0u;
+        const uint32_t old = a.accumulate ? status0 : 0u;
         if (tid == 0) bad = 0u;
         __syncthreads();
-        const int w = tid >> 6, lane = tid & 63;
-        for (int64_t rec0 = w; rec0 < a.n_rec; rec0 += 16) {
+        for (int64_t rec0 = w; rec0 < a.n_rec; rec0 += 4 * nw) {
             double s4[4];
-            record_norm2_x4(a.parts, a.parts_stride, a.n_parts, rec0, 4, a.n_rec, lane, s4);
-            if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t rec = rec0 + 4 * j;
-                    if (rec >= a.n_rec) break;
-                    const double s = s4[j];
-                    const double n = sqrt(s);
-                    const double c = (n <= a.C) ? 1.0 : a.C / n;
-                    if (!isfinite(s)) atomicOr(&bad, 1u);
-                    cs[rec] = (float)c;
-                    if (blockIdx.x == 0 && l == 0) {
-                        a.n_ws[rec] = (float)n;
-                        a.c_ws[rec] = (float)c;
-                        if (a.n_user) a.n_user[rec] = (float)n;
-                        if (a.c_user) a.c_user[rec] = (float)c;
-                    }
+            if (rec0 == w)
+                record_norm2_x4_from(pv, a.parts, a.parts_stride, a.n_parts, rec0, nw, a.n_rec, lane, s4);
+            else
+                record_norm2_x4(a.parts, a.parts_stride, a.n_parts, rec0, nw, a.n_rec, lane, s4);
+            // every lane holds the four sums; lane j < 4 finishes record rec0 + j nw
+            const int64_t rec = rec0 + (int64_t)lane * nw;
+            if (lane < 4 && rec < a.n_rec) {
+                const double s = lane == 0 ? s4[0] : lane == 1 ? s4[1] : lane == 2 ? s4[2] : s4[3];
+                const double n = sqrt(s);
+                const double c = (n <= a.C) ? 1.0 : a.C / n;
+                if (!isfinite(s)) atomicOr(&bad, 1u);
+                cs[rec] = (float)c;
+                if (blockIdx.x == 0 && l == 0) {
+                    a.n_ws[rec] = (float)n;
+                    a.c_ws[rec] = (float)c;
+                    if (a.n_user) a.n_user[rec] = (float)n;
+                    if (a.c_user) a.c_user[rec] = (float)c;
                 }
             }
         }
@@ -85,7 +103,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
         skip = (old | bad) != 0u;
         cf = cs;
     } else {
-        skip = *a.status != 0u;
+        skip = status0 != 0u;
     }
     if (skip || !active) return;
 
@@ -141,13 +159,42 @@ __global__ __launch_bounds__(256) void k_finalize(FinalizeArgs a) {
     }
 }
 
+// compute units of the current device (cached per device)
+static int64_t compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s) {
     int64_t max_n = 0;
-    for (int l = 0; l < a.n_layers; ++l) max_n = std::max<int64_t>(max_n, a.off[l + 1] - a.off[l]);
+    bool vec = true;
+    for (int l = 0; l < a.n_layers; ++l) {
+        const int64_t n_l = a.off[l + 1] - a.off[l];
+        max_n = std::max<int64_t>(max_n, n_l);
+        const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.src[l]) |
+                               reinterpret_cast<uintptr_t>(a.params[l]);
+        if (n_l < 4 || (n_l & 3) != 0 || (a.off[l] & 3) != 0 || (ptrs & 15u) != 0) vec = false;
+    }
     if (max_n == 0) return hipSuccess;
-    const dim3 grid((unsigned)((max_n + 1023) / 1024), a.n_layers);
-    if (clip_inside) hipLaunchKernelGGL(k_finalize<true>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_finalize<false>, grid, dim3(256), 0, s, a);
+    // about one workgroup per compute unit: chunks per layer so that the layers fill the
+    // chip, wavefronts per workgroup so that the chunks cover a layer
+    const int64_t n_cu = compute_units();
+    const int64_t max_f4 = (max_n + 3) / 4;
+    const int64_t per_layer = std::max<int64_t>(1, n_cu / a.n_layers);
+    const int64_t nw = std::min<int64_t>(kFinalMaxThreads / 64, (max_f4 + 64 * per_layer - 1) / (64 * per_layer));
+    const int64_t threads = 64 * nw;
+    const dim3 grid((unsigned)((max_f4 + threads - 1) / threads), a.n_layers);
+    if (clip_inside && vec) hipLaunchKernelGGL((k_finalize<true, true>), grid, dim3((unsigned)threads), 0, s, a);
+    else if (clip_inside) hipLaunchKernelGGL((k_finalize<true, false>), grid, dim3((unsigned)threads), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((k_finalize<false, true>), grid, dim3((unsigned)threads), 0, s, a);
+    else hipLaunchKernelGGL((k_finalize<false, false>), grid, dim3((unsigned)threads), 0, s, a);
     return hipGetLastError();
 }
 
