@@ -333,6 +333,11 @@ def secondary(args, w, torch, dev, dp, datagen):
     nb, nf = work["norms"]
     nb *= w.n_phys
     nf *= w.n_phys
+    try:
+        ach = achievable_hbm(torch, dev, dp)
+    except torch.cuda.OutOfMemoryError:
+        ach = None
+    norm_gbs = nb / (phase["norms"] * 1e-3) / 1e9
     line = {"metric": METRIC, "value": w.logical_B / (ms * 1e-3), "unit": "records/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": datagen.configs.DTYPE_NAMES[w.dtype],
@@ -342,9 +347,10 @@ def secondary(args, w, torch, dev, dp, datagen):
                        "parallelism": "single GPU", "note": note,
                        "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
             "phases_ms": phase,
-            "norms_roofline": {"hbm_GBps": nb / (phase["norms"] * 1e-3) / 1e9,
-                               "hbm_frac": nb / (phase["norms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "norms_roofline": {"hbm_GBps": norm_gbs, "hbm_frac": norm_gbs / HBM_PEAK_GBS,
+                               "frac_of_achievable": norm_gbs / ach["read_gbs"] if ach else None,
                                "TFLOPs": nf / (phase["norms"] * 1e-3) / 1e12},
+            "hbm_achievable": ach,
             "clipped_sum_roofline": sum_roofline(work, w, phase),
             "clipped_sum_bytes": work["clipped_sum"][0] * w.n_phys}
     print(json.dumps(line), flush=True)
@@ -556,6 +562,28 @@ def int8_line(args, torch, dev, dp):
     print(json.dumps(line), flush=True)
 
 
+def achievable_hbm(torch, dev, dp, mib=2048, reps=10):
+    """The HBM read rate that a plain streaming read with 16-byte loads reaches on this device
+    (dpsgd_hbm_read over a 2 GiB buffer, best of `reps` launches timed with HIP events): the
+    measured reference beside the vendor peak."""
+    nbytes = mib << 20
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(dp.HBM_READ_SINK_WORDS, dtype=torch.int32, device=dev)
+    dp.hbm_read(x.data_ptr(), nbytes, sink.data_ptr())
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dp.hbm_read(x.data_ptr(), nbytes, sink.data_ptr())
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    del x, sink
+    return {"read_gbs": nbytes / best / 1e9,
+            "how": f"dpsgd_hbm_read: streaming 16-byte loads over {mib} MiB, best of {reps}"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -691,6 +719,9 @@ def main():
         if (tr.get("kernel_phase") == dom and tr.get("workload") == w.name
                 and tr.get("src_hash") == kernel_src_hash()):
             roof["traffic"] = tr.get("bytes_per_launch")
+    if roof["unit"] == "GB/s":
+        roof["achievable"] = achievable_hbm(torch, dev, dp)
+        roof["frac_of_achievable"] = roof["achieved"] / roof["achievable"]["read_gbs"]
     roof["kernel"] = {"norms": "k_norm_direct (ghost_norm, direct path)",
                       "clipped_sum": "clipped_sum", "noise": "k_noise"}[dom]
     roof["algorithmic_bytes"] = nbytes

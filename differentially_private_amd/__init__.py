@@ -36,7 +36,7 @@ EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
            "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_ws_segments", "dpsgd_norms", "dpsgd_clip",
            "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_status",
            "dpsgd_layer_norm2",
-           "dpsgd_philox_raw", "dpsgd_poisson_ws_bytes", "dpsgd_poisson_sample",
+           "dpsgd_philox_raw", "dpsgd_hbm_read", "dpsgd_poisson_ws_bytes", "dpsgd_poisson_sample",
            "dpsgd_rdp_sampled_gaussian", "dpsgd_rdp_to_epsilon", "dpsgd_gaussian_pair_delta",
            "dpsgd_gaussian_pair_epsilon", "dpsgd_i8_pitch", "dpsgd_i8_plan_create",
            "dpsgd_i8_plan_destroy", "dpsgd_i8_quantize_weight", "dpsgd_i8_set_records",
@@ -102,6 +102,7 @@ def load():
         "dpsgd_status": (ctypes.c_int, [P, P, P]),
         "dpsgd_layer_norm2": (ctypes.c_int, [P, I64, I32, I32, P, P, P]),
         "dpsgd_philox_raw": (ctypes.c_int, [U64, U64, U64, U64, P, P]),
+        "dpsgd_hbm_read": (ctypes.c_int, [P, ctypes.c_int64, P, P]),
         "dpsgd_poisson_ws_bytes": (I64, [I64]),
         "dpsgd_poisson_sample": (ctypes.c_int, [U64, U64, D, I64, P, P, P, P, P]),
         "dpsgd_rdp_sampled_gaussian": (ctypes.c_int, [D, D, PD, I32, PD]),
@@ -292,6 +293,14 @@ def status(plan: Plan, ws, stream=None) -> int:
 def layer_norm2(plan: Plan, n_records: int, l0: int, l1: int, ws, out, stream=None):
     _check(load().dpsgd_layer_norm2(plan.handle, n_records, l0, l1, _ptr(ws), _ptr(out),
                                     _stream(stream)))
+
+
+HBM_READ_SINK_WORDS = 8192
+
+
+def hbm_read(buf, nbytes: int, sink, stream=None):
+    """dpsgd_hbm_read: streaming read of nbytes of buf; sink holds HBM_READ_SINK_WORDS uint32."""
+    _check(load().dpsgd_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
 
 
 def philox_raw(seed: int, step: int, first_block: int, n_blocks: int, out, stream=None):

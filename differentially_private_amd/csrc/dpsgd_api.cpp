@@ -526,6 +526,10 @@ struct I8PlanImpl {
 int64_t i8_pitch(int64_t k) { return (k + 63) / 64 * 64; }
 
 
+namespace dpsgd {
+hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+}
+
 extern "C" {
 
 int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_bytes) {
@@ -844,6 +848,15 @@ int dpsgd_layer_norm2(const dpsgd_plan* p, int64_t n_rec, int32_t l0, int32_t l1
         hipError_t e = launch_layer_norm2(a, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "layer norm launch");
     }
+    return DPSGD_OK;
+}
+
+int dpsgd_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(DPSGD_ERR_INVALID_ARG, "buf or sink is NULL");
+    if (bytes <= 0 || bytes % 16 != 0) return fail(DPSGD_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (!ptr_aligned16(buf)) return fail(DPSGD_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+    hipError_t e = dpsgd::launch_hbm_read(buf, bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hbm_read launch");
     return DPSGD_OK;
 }
 

@@ -342,6 +342,16 @@ int dpsgd_layer_norm2(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int
 int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_t n_blocks,
                      uint32_t* dev_out, void* stream);
 
+/* Measurement aid (not a step of the method): a plain streaming read of `bytes`
+ * bytes at device pointer `buf` (16-byte aligned, bytes a positive multiple of
+ * 16), the reference for the HBM bandwidth that ordinary 16-byte loads reach on
+ * this device.  Writes DPSGD_HBM_READ_SINK_WORDS words to device pointer `sink`
+ * (caller-owned): the XOR of all of them equals the XOR of every 32-bit word of
+ * the buffer.  Asynchronous on `stream`; argument errors are returned before any
+ * launch. */
+#define DPSGD_HBM_READ_SINK_WORDS 8192
+int dpsgd_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* dpsgd_error_string(int code);
 

@@ -237,3 +237,13 @@ def test_i8_entry_points_reject_before_launch():
         with pytest.raises(dp.DpsgdError):
             dp.i8_quantize_weight(*args, stream=0)
     assert lib.dpsgd_i8_pitch(64) == 64
+
+
+def test_hbm_read_rejects_before_launch():
+    """The streaming-read measurement aid checks its arguments on the host (no GPU is touched)."""
+    fake = 1 << 40          # never dereferenced: every case below fails validation first
+    for buf, nbytes, sink in [(0, 16, fake), (fake, 16, 0), (fake, 0, fake), (fake, -16, fake),
+                              (fake, 24, fake), (fake + 8, 16, fake)]:
+        with pytest.raises(dp.DpsgdError) as e:
+            dp.hbm_read(buf, nbytes, sink, stream=0)
+        assert e.value.code == dp.ERR_INVALID_ARG
