@@ -13,6 +13,8 @@
 //    pairs weighted by 2.
 // Each wavefront writes one fp32 partial per (record, tile): the partials of a
 // record depend only on that record's rows, so the norms are batch-invariant.
+#include <algorithm>
+
 #include "tile_direct.h"
 
 namespace dpsgd {
@@ -318,6 +320,217 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
     }
 }
 
+// ---- Gram path, one workgroup per (record, layer) when T <= 256 ----
+//
+// Same inputs as k_norm_gram_copy (bf16, 16-byte aligned rows, d_in and d_out multiples
+// of 32), with the nb (nb + 1) / 2 upper-triangle pairs of 64-token blocks of one
+// (record, layer) in a single workgroup, so each token row is copied into LDS once per
+// feature step rather than once per block pair it belongs to, and the copies run up to
+// 7 steps ahead (stages of all 4 nb 16-row blocks, 4 nb KB each, as many as fit in
+// 144 KB, at most 8).  Wavefronts:
+//  - one per off-diagonal pair (tb < sb): the full 64 x 64 Gram blocks of A and G,
+//    formed exactly as a k_norm_gram_copy wavefront forms them;
+//  - one per two diagonal blocks: only the 10 upper-triangle 16 x 16 tiles of each
+//    64 x 64 diagonal block (the Gram is symmetric), the strictly upper ones doubled in
+//    the Hadamard sum.
+// For nb = 4 that is 6 + 2 = 8 wavefronts, two per SIMD.  Each wavefront issues the
+// same number of 1 KB copies per step (blocks w * per + j mod 4 nb; a block may be copied
+// twice, with the same bytes to the same place), so one vmcnt value describes every
+// wavefront's copies in flight.  Partials go to the slots k_norm_gram uses.
+constexpr int kGramRecMaxNb = 4;                 // T <= 256
+constexpr int kGramRecWaves = 8;                 // for nb = 4
+constexpr int kGramRecMaxLds = 144 * 1024;
+constexpr int kGramRecMaxStages = 8;
+// a group of two steps needs both copied before the previous group's barrier: 4 stages or more
+static_assert(kGramRecMaxLds / (4 * kGramRecMaxNb * 1024) >= 4 && kGramRecMaxStages >= 4, "stages");
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 28]
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+#define DPSGD_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        DPSGD_VM(1) DPSGD_VM(2) DPSGD_VM(3) DPSGD_VM(4) DPSGD_VM(5) DPSGD_VM(6) DPSGD_VM(7)
+        DPSGD_VM(8) DPSGD_VM(9) DPSGD_VM(10) DPSGD_VM(11) DPSGD_VM(12) DPSGD_VM(13) DPSGD_VM(14)
+        DPSGD_VM(15) DPSGD_VM(16) DPSGD_VM(17) DPSGD_VM(18) DPSGD_VM(19) DPSGD_VM(20) DPSGD_VM(21)
+        DPSGD_VM(22) DPSGD_VM(23) DPSGD_VM(24) DPSGD_VM(25) DPSGD_VM(26) DPSGD_VM(27) DPSGD_VM(28)
+#undef DPSGD_VM
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// upper-triangle 16 x 16 tile (mi <= ni) of a 64 x 64 diagonal block -> 0..9
+__host__ __device__ constexpr int tri_tile(int mi, int ni) { return mi * 4 - mi * (mi - 1) / 2 + (ni - mi); }
+
+__global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs args, int n_stages) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds_rec[];
+    const GramLayer& L = args.L[blockIdx.y];
+    const int64_t rec = blockIdx.x;
+    const int64_t T = args.T;
+    const int nb = args.nb;                 // 64-token blocks (1..4)
+    const int n_off = nb * (nb - 1) / 2;    // off-diagonal pairs: waves 0 .. n_off - 1
+    const int n16 = 4 * nb;                 // 16-row blocks per stage (rows past T repeat row T - 1)
+    const int stage_elems = n16 * 512;      // 1 KB per 16-row block
+    const int nw = (int)(blockDim.x >> 6);  // n_off + ceil(nb / 2)
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const bool off_wave = w < n_off;
+    // off-diagonal wave: pair (tb, sb), tb < sb, in row-major order; diagonal wave: blocks
+    // d0 = 2 (w - n_off) and d0 + 1 (if < nb)
+    int tb = 0, sb = 0;
+    if (off_wave) {
+        int rem = w;
+        while (rem >= nb - 1 - tb) {
+            rem -= nb - 1 - tb;
+            ++tb;
+        }
+        sb = tb + 1 + rem;
+    }
+    const int d0 = 2 * (w - n_off);
+    const bool has_d1 = !off_wave && d0 + 1 < nb;
+
+    // copies: wave w issues blocks (w * per + j) mod n16, j < per; lane L fetches chunk L / 16
+    // of row L % 16 of the block (row clamped to T - 1)
+    const int per = (n16 + nw - 1) / nw;    // 1 .. 4
+    uint32_t offa[4], offg[4], dsto[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int b = (w * per + j) % n16;
+        int64_t t = 16 * (int64_t)b + (lane & 15);
+        if (t > T - 1) t = T - 1;
+        offa[j] = (uint32_t)((t * L.d_in + 8 * (lane >> 4)) * 2);
+        offg[j] = (uint32_t)((t * L.d_out + 8 * (lane >> 4)) * 2);
+        dsto[j] = (uint32_t)(b * 1024);
+    }
+    const int nA = L.d_in / kGramK, nG = L.d_out / kGramK;
+    const int total = nA + nG;
+    const char* recA = static_cast<const char*>(L.A) + rec * T * L.d_in * 2;
+    const char* recG = static_cast<const char*>(L.G) + rec * T * L.d_out * 2;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_rec));
+    auto issue = [&](int s, int st) {
+        const uint32_t dst = lds0 + (uint32_t)(st * stage_elems * 2);
+        const bool a_step = s < nA;
+        const char* base = a_step ? recA + (int64_t)s * kGramK * 2 : recG + (int64_t)(s - nA) * kGramK * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < per) copy16(base, a_step ? offa[j] : offg[j], dst + dsto[j]);
+    };
+
+    // The copy pipeline: feature steps in groups of two (one at the end of a phase) per barrier,
+    // the A steps then the G steps, so that within a group the second step's LDS reads can
+    // overlap the first step's MFMAs.  At a group's barrier every earlier step is retired and
+    // its stage is refilled with the next step to copy.  Each role runs its own copy of the
+    // loop so that its accumulators live only there; both pass the same barriers.
+    const int n = n_stages;
+    auto pipeline = [&](auto&& step_a, auto&& step_g) {
+        int next = min(n, total);   // next step to copy
+        for (int k = 0; k < next; ++k) issue(k, k);
+        int s = 0;
+        auto group = [&](int m, auto&& compute) {
+            wait_vm(per * (next - s - m));   // steps s .. s + m - 1 done, later ones in flight
+            __syncthreads();
+            const int lim = min(total, s + n);
+            for (; next < lim; ++next) issue(next, next % n);
+            compute();
+            s += m;
+        };
+        auto stage = [&](int k) { return lds_rec + (k % n) * stage_elems; };
+        while (s + 1 < nA) group(2, [&] { step_a(stage(s)); step_a(stage(s + 1)); });
+        if (s < nA) group(1, [&] { step_a(stage(s)); });
+        while (s + 1 < total) group(2, [&] { step_g(stage(s)); step_g(stage(s + 1)); });
+        if (s < total) group(1, [&] { step_g(stage(s)); });
+    };
+    float* parts = args.parts + rec * args.parts_stride + L.part_off;
+
+    // Hadamard sums below: lane (g, c) holds rows 4g + r, column c of each 16 x 16 tile
+    if (off_wave) {
+        f32x4 ga[16], gg[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            ga[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto step = [&](const uint16_t* S, f32x4 (&acc)[16]) {
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * tb + mi) * 512 + 8 * lane);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                bv[ni] = *reinterpret_cast<const u32x4*>(S + (4 * sb + ni) * 512 + 8 * lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[4 * mi + ni] = mfma_bf16(av[mi], bv[ni], acc[4 * mi + ni]);
+        };
+        pipeline([&](const uint16_t* S) { step(S, ga); }, [&](const uint16_t* S) { step(S, gg); });
+        float sum = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t t = (int64_t)64 * tb + 16 * mi + 4 * g + r;
+                    const int64_t u = (int64_t)64 * sb + 16 * ni + c;
+                    const float v = ga[4 * mi + ni][r] * gg[4 * mi + ni][r];
+                    sum += (t < T && u < T) ? v : 0.f;
+                }
+        sum = wave_sum(sum);
+        if (lane == 0) parts[tb * nb - tb * (tb - 1) / 2 + (sb - tb)] = 2.f * sum;
+    } else {
+        // tiles 0..9 of block d0, 10..19 of block d1 = min(d0 + 1, nb - 1) (computed, and
+        // dropped, when d0 is the last block: no branch between the loads and the MFMAs)
+        const int d1 = has_d1 ? d0 + 1 : d0;
+        f32x4 da[20], dg[20];
+#pragma unroll
+        for (int i = 0; i < 20; ++i) {
+            da[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto step = [&](const uint16_t* S, f32x4 (&acc)[20]) {
+            u32x4 av[2][4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                av[0][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d0 + mi) * 512 + 8 * lane);
+                av[1][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d1 + mi) * 512 + 8 * lane);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = mi; ni < 4; ++ni) {
+                        const int q = 10 * e + tri_tile(mi, ni);
+                        acc[q] = mfma_bf16(av[e][mi], av[e][ni], acc[q]);
+                    }
+        };
+        pipeline([&](const uint16_t* S) { step(S, da); }, [&](const uint16_t* S) { step(S, dg); });
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (e == 1 && !has_d1) break;
+            const int d = d0 + e;
+            float sum = 0.f;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = mi; ni < 4; ++ni) {
+                    const int q = 10 * e + tri_tile(mi, ni);
+                    float part = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t t = (int64_t)64 * d + 16 * mi + 4 * g + r;
+                        const int64_t u = (int64_t)64 * d + 16 * ni + c;
+                        const float v = da[q][r] * dg[q][r];
+                        part += (t < T && u < T) ? v : 0.f;
+                    }
+                    sum += (mi == ni) ? part : 2.f * part;
+                }
+            sum = wave_sum(sum);
+            if (lane == 0) parts[d * nb - d * (d - 1) / 2] = sum;
+        }
+    }
+}
+
 hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s) {
     int gx = 1;
     for (int l = 0; l < a.n_layers; ++l) {
@@ -345,6 +558,14 @@ hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s) {
         const GramLayer& d = a.L[l];
         copy = copy && d.vec_a && d.vec_g && d.d_in % kGramK == 0 && d.d_out % kGramK == 0 &&
                a.T * (int64_t)std::max(d.d_in, d.d_out) * 2 < ((int64_t)1 << 31);
+    }
+    if (copy && a.nb <= kGramRecMaxNb) {
+        const int n_stages = std::min(kGramRecMaxStages, kGramRecMaxLds / (4 * a.nb * 1024));
+        const size_t lds = (size_t)n_stages * 4 * a.nb * 1024;
+        const int nw = a.nb * (a.nb - 1) / 2 + (a.nb + 1) / 2;
+        hipLaunchKernelGGL(k_norm_gram_rec, dim3((unsigned)a.n_rec, a.n_layers), dim3(64 * nw), lds, s, a,
+                           n_stages);
+        return hipGetLastError();
     }
     if (copy) {
         const int64_t nb = (a.T + kGramB - 1) / kGramB;

@@ -1,8 +1,9 @@
 """GPU parity of the Gram-path ghost norms of bf16 layers against the oracle.
 
-The copy kernel (rows 16-byte aligned, d_in and d_out multiples of 32) takes 128-token block
-pairs; these cases put T off every block multiple (50, 200, 300), give 1 to 17 records (the
-records of one block-pair set are spread over XCDs by record index mod 8), and mix layer shapes.
+With rows 16-byte aligned and d_in, d_out multiples of 32, records of at most 256 tokens take the
+one-workgroup-per-record kernel (off-diagonal 64-token block pairs and pairs of diagonal blocks
+as wavefronts) and longer ones the 128-token block-pair kernel; these cases put T off every block
+multiple (50, 200, 300), give 1 to 17 records, and mix layer shapes.
 Per-layer squared norms are compared with the oracle (relative 2e-3, bf16 inputs) and with the
 direct path on the same data; integer inputs small enough for exact fp32 sums are compared bit
 for bit.  Misaligned rows take the register kernel and must agree as well.
