@@ -56,6 +56,7 @@ def _load():
             "orc_gauss": (None, [_U64, _U64, _U64, _I64, _P]),
             "orc_add_noise": (None, [_P, _I64, _U64, _D, _D, _U64, _U64]),
             "orc_num_threads": (ctypes.c_int, []),
+            "orc_set_num_threads": (None, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -68,6 +69,11 @@ def _load():
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops."""
+    _load().orc_set_num_threads(n)
 
 
 def _dtype_of(x: np.ndarray) -> int:

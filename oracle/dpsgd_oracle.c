@@ -230,3 +230,6 @@ void orc_add_noise(double* S, int64_t n, uint64_t first_e, double sigma, double 
 
 /* Threads the oracle's parallel loops use (for reporting). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
+
+/* Threads for the oracle's later parallel loops (for a single-thread timing). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
