@@ -3,7 +3,8 @@
 With rows 16-byte aligned and d_in, d_out multiples of 32, records of at most 256 tokens take the
 one-workgroup-per-record kernel (off-diagonal 64-token block pairs and pairs of diagonal blocks
 as wavefronts) and longer ones the 128-token block-pair kernel; these cases put T off every block
-multiple (50, 200, 300), give 1 to 17 records, and mix layer shapes.
+multiple (50, 129, 150, 200, 300: one, three and four 64-token blocks, where three leaves a
+diagonal wavefront with a single block), give 1 to 17 records, and mix layer shapes.
 Per-layer squared norms are compared with the oracle (relative 2e-3, bf16 inputs) and with the
 direct path on the same data; integer inputs small enough for exact fp32 sums are compared bit
 for bit.  Misaligned rows take the register kernel and must agree as well.
@@ -53,6 +54,8 @@ def layer_norm2(shapes, T, B, As, Gs, path, shift=False):
 @pytest.mark.parametrize("T,shapes,B", [
     (50, ((32, 64), (96, 32)), 3),
     (128, ((64, 64),), 9),
+    (150, ((64, 96), (96, 32)), 4),
+    (129, ((32, 64),), 3),
     (200, ((64, 96), (32, 32)), 5),
     (256, ((128, 256),), 17),
     (300, ((32, 64), (64, 32)), 2),
