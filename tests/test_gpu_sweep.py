@@ -1,0 +1,110 @@
+"""Seeded random sweeps of the HIP path against the oracle.
+
+- The fused tail of plans whose layers all keep their gradient blocks (direct path, SUM_STORED): random layer
+  shapes and counts give workgroups of one to eight wavefronts; layers whose sizes are not
+  multiples of 4 take the element-wise variant; more than 1024 records put the clip factors in a
+  separate launch; more than 48 layers split the tail into several launches.  Norms and clip
+  factors (relative 1e-5 fp32 / 2e-3 bf16), the pre-noise sum and the noised sum (relative
+  Frobenius, same bounds) are compared.
+- The bf16 Gram path for records of at most 256 tokens (one workgroup per record and layer):
+  random T, widths (multiples of 32) and record counts; per-layer squared norms against the
+  oracle.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import datagen  # noqa: E402
+import differentially_private_amd as dp  # noqa: E402
+import oracle  # noqa: E402
+from _helpers import TOL, flat, gpu_step, host_inputs, max_rel, rel_err, to_device  # noqa: E402
+from datagen import BF16, F32  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _stored_case(i):
+    rng = np.random.default_rng(7000 + i)
+    dtype = F32 if i % 2 == 0 else BF16
+    n_layers = int(rng.integers(1, 7))
+    layers = []
+    for _ in range(n_layers):
+        if rng.random() < 0.5:   # sizes that are multiples of 4 (vector tail) or not
+            layers.append((int(4 * rng.integers(1, 25)), int(4 * rng.integers(1, 25))))
+        else:
+            layers.append((int(rng.integers(1, 90)), int(rng.integers(1, 90))))
+    return dict(dtype=dtype, layers=tuple(layers), B=int(rng.integers(1, 21)), T=int(rng.integers(1, 49)),
+                seed=8000 + i)
+
+
+STORED_CASES = [_stored_case(i) for i in range(12)] + [
+    dict(dtype=F32, layers=((4, 4), (3, 5)), B=1100, T=2, seed=9001),        # clip factors outside
+    dict(dtype=F32, layers=tuple((4, 8) if l % 3 else (5, 3) for l in range(50)), B=5, T=3,
+         seed=9002),                                                          # two tail launches
+    dict(dtype=BF16, layers=((768, 8), (8, 768), (1024, 8)), B=7, T=40, seed=9003),  # wide layers
+]
+
+
+@pytest.mark.parametrize("case", range(len(STORED_CASES)))
+def test_stored_tail_sweep(case):
+    c = STORED_CASES[case]
+    w = datagen.Workload(name=f"sweep{case}", layers=c["layers"],
+                         layer_names=tuple(f"l{l}" for l in range(len(c["layers"]))), dtype=c["dtype"],
+                         B=c["B"], logical_B=c["B"], T=c["T"], C=1.0, sigma=0.7, data_seed=c["seed"])
+    say("stored sweep", case, "dtype", c["dtype"], "B", c["B"], "T", c["T"], "layers", len(c["layers"]),
+        c["layers"][:4])
+    As, Gs = host_inputs(w)
+    ref = oracle.step(As, Gs, w.C, w.sigma, 3, 11)
+    r = gpu_step(w, As, Gs, DEV, seed=3, step=11, path=dp.PATH_DIRECT, sum_policy=dp.SUM_STORED)
+    tol = TOL[w.dtype]
+    en, ec = max_rel(r["n"], ref["n"]), max_rel(r["c"], ref["c"])
+    eS = rel_err(flat(r["out"]), flat(ref["S_noised"]))
+    r0 = gpu_step(w, As, Gs, DEV, seed=3, step=11, path=dp.PATH_DIRECT, sum_policy=dp.SUM_STORED,
+                  flags=dp.NO_NOISE)
+    e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
+    say(f"  norm {en:.2e} clip {ec:.2e} noised {eS:.2e} pre-noise {e0:.2e}")
+    assert r["status"] == dp.OK and r0["status"] == dp.OK
+    assert en <= tol and ec <= tol and eS <= tol and e0 <= tol
+
+
+def _gram_case(i):
+    rng = np.random.default_rng(7100 + i)
+    n_layers = int(rng.integers(1, 4))
+    layers = tuple((int(32 * rng.integers(1, 9)), int(32 * rng.integers(1, 9))) for _ in range(n_layers))
+    return dict(layers=layers, B=int(rng.integers(1, 7)), T=int(rng.integers(1, 257)), seed=8100 + i)
+
+
+GRAM_CASES = [_gram_case(i) for i in range(10)]
+
+
+@pytest.mark.parametrize("case", range(len(GRAM_CASES)))
+def test_gram_per_record_sweep(case):
+    c = GRAM_CASES[case]
+    shapes, B, T = c["layers"], c["B"], c["T"]
+    w = datagen.Workload(name=f"gsweep{case}", layers=shapes,
+                         layer_names=tuple(f"l{l}" for l in range(len(shapes))), dtype=BF16, B=B,
+                         logical_B=B, T=T, C=1.0, sigma=0.0, data_seed=c["seed"])
+    say("gram sweep", case, "T", T, "B", B, "layers", shapes)
+    As, Gs = host_inputs(w)
+    want = np.stack([oracle.layer_norm2(a, g) for a, g in zip(As, Gs)])
+    plan = dp.Plan(shapes, BF16, B, T, dp.PATH_GRAM)
+    ws = plan.workspace(DEV)
+    dA = [to_device(a, DEV) for a in As]
+    dG = [to_device(g, DEV) for g in Gs]
+    dp.ws_init(plan, ws)
+    dp.norms(plan, B, 0, len(shapes), dA, dG, ws)
+    out = torch.empty(len(shapes) * B, dtype=torch.float32, device=DEV)
+    dp.layer_norm2(plan, B, 0, len(shapes), ws, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(len(shapes), B).astype(np.float64)
+    e = max_rel(got, want)
+    say(f"  rel {e:.2e}")
+    assert e <= TOL[BF16]
