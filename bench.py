@@ -252,11 +252,21 @@ def secondary(args, w, torch, dev, dp, datagen):
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     phase = {"norms": 0.0, "rest_of_step": 0.0}
     note = ""
+    n_cycle = 1
     if w.n_phys * in_bytes < free - (8 << 30):
         batches = [device_inputs(w, datagen, torch, dev, p * w.B, w.B) for p in range(w.n_phys)]
+        # one physical batch: the timed steps cycle through N_SETS distinct batches when they fit,
+        # so that no step re-reads inputs a previous step left in the last-level cache
+        cycle = [batches]
+        if w.n_phys == 1 and N_SETS * in_bytes < (free - (8 << 30)) // 2:
+            cycle += [[device_inputs(w, datagen, torch, dev, k * w.B, w.B)] for k in range(1, N_SETS)]
+        turn = [0]
+        n_cycle = len(cycle)
 
         def step():
-            for p, (As, Gs) in enumerate(batches):
+            bs = cycle[turn[0] % len(cycle)]
+            turn[0] += 1
+            for p, (As, Gs) in enumerate(bs):
                 flags = (dp.NO_NOISE if w.n_phys > 1 else 0) | (dp.ACCUMULATE if p else 0)
                 last = w.n_phys == 1
                 dp.step(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, flags=flags,
@@ -362,7 +372,7 @@ def secondary(args, w, torch, dev, dp, datagen):
                        "records_per_step": w.logical_B, "physical_batches": w.n_phys, "tokens": w.T,
                        "parallelism": "single GPU", "note": note,
                        "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
-            "phases_ms": phase,
+            "phases_ms": phase, "input_batches": n_cycle,
             "norms_roofline": {"hbm_GBps": norm_gbs, "hbm_frac": norm_gbs / HBM_PEAK_GBS,
                                "frac_of_achievable": norm_gbs / ach["read_gbs"] if ach else None,
                                "TFLOPs": nf / (phase["norms"] * 1e-3) / 1e12},
@@ -372,6 +382,7 @@ def secondary(args, w, torch, dev, dp, datagen):
     print(json.dumps(line), flush=True)
 
 
+N_SETS = 4   # distinct input batches the headline's timed steps cycle through
 I8_PEAK_TOPS = 5000.0   # dense INT8 MFMA, ops/s x 1e-12
 
 
@@ -670,6 +681,10 @@ def main():
     out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
     L = w.n_layers
     stream = torch.cuda.current_stream()
+    # the timed steps cycle through N_SETS distinct batches (records k B .. k B + B - 1 of the
+    # generator), so that no step re-reads inputs a previous step left in the last-level cache
+    sets = [(As, Gs)] + ([device_inputs(w, datagen, torch, dev, k * w.B, w.B) for k in range(1, N_SETS)]
+                         if args.mode == "step" else [])
 
     if args.mode == "kernel":
         for _ in range(args.warmup + args.steps):
@@ -681,35 +696,41 @@ def main():
 
     theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
              if args.descent else None)
-    call = dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, params=theta,
-                       lr=DESCENT_LR, normalizer=DESCENT_L)
-    for _ in range(args.warmup):
-        call()
+    calls = [dp.StepCall(plan, A, G, out, ws, w.C, w.sigma, w.noise_seed, 0, params=theta,
+                         lr=DESCENT_LR, normalizer=DESCENT_L) for A, G in sets]
+    for i in range(max(args.warmup, len(calls))):
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
     assert dp.status(plan, ws) == dp.OK
 
-    # timed region 1: K whole steps (dpsgd_step: norms -> clip -> clipped sum -> noise)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        call()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
+    # timed region 1: K whole steps (dpsgd_step: norms -> clip -> clipped sum -> noise), each on
+    # the next batch of the cycle
+    def timed_steps(cs):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            cs[i % len(cs)]()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop), time.perf_counter() - t0
+    gpu_ms, wall = timed_steps(calls)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     assert dp.status(plan, ws) == dp.OK
+    # the same batch every step, for comparison (its inputs partly stay in the last-level cache)
+    gpu1, wall1 = timed_steps(calls[:1])
+    same_ms = max(gpu1, wall1 * 1e3) / args.steps
 
     # timed region 2: the dominant kernel (the norm launch of the same step, same buffers),
     # bracketed by HIP events on the stream it runs on
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    for e0, e1 in evs:
+    for i, (e0, e1) in enumerate(evs):
+        A, G = sets[i % len(sets)]
         e0.record(stream)
-        dp.norms(plan, w.B, 0, L, As, Gs, ws)
+        dp.norms(plan, w.B, 0, L, A, G, ws)
         e1.record(stream)
     torch.cuda.synchronize()
     phase_ms = {"norms": sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps}
@@ -760,6 +781,9 @@ def main():
         "roofline": roof, "cpu_baseline": cpu,
         "phases_ms": phase_ms, "gpu_ms_per_step": gpu_ms / args.steps,
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "input_batches": len(sets),
+        "same_batch": {"value": w.B / (same_ms * 1e-3), "ms_per_step": same_ms,
+                       "note": "every timed step on one batch; its inputs partly stay in the last-level cache"},
     }
     print(json.dumps(line), flush=True)
     if args.manifest:
