@@ -80,13 +80,28 @@ def device_inputs(w, datagen, torch, dev, first, n):
 NORM_KERNEL_SOURCES = ("ghost_norm.hip", "tile_direct.h", "device_common.h", "internal.h")
 
 
-def kernel_src_hash() -> str:
+# sources the INT8 forward's kernels are compiled from (same rule for its traffic record)
+I8_KERNEL_SOURCES = ("int8_forward.hip", "int8.h", "device_common.h", "internal.h")
+
+
+def kernel_src_hash(names=NORM_KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in NORM_KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "differentially_private_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def stored_i8_traffic():
+    """HBM-side bytes per k_i8_gemm launch (mean over the OPT-125M layer shapes) from rocprofv3
+    FETCH_SIZE / WRITE_SIZE, scaled by a plain copy of known size; None once the kernel sources
+    differ from the ones it was measured on."""
+    path = os.path.join(ROOT, "profiles", "int8_gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    tr = json.load(open(path))
+    return tr.get("bytes_per_launch") if tr.get("src_hash") == kernel_src_hash(I8_KERNEL_SOURCES) else None
 
 
 def cpu_baseline(w, seconds):
@@ -490,6 +505,7 @@ def int8_line(args, torch, dev, dp):
     gemm_ms = 0.0
     reps = max(1, args.steps // 10)
     launches = 0
+    abytes = 0   # codes + weight codes read, fp16 outputs written (outlier corrections aside)
     for _ in range(reps):
         for L in m["layers"]:
             dp.i8_route(plan, ws, n, B, L["A"], L["K"], 6.0, stream)
@@ -500,13 +516,15 @@ def int8_line(args, torch, dev, dp):
             torch.cuda.synchronize()
             gemm_ms += e0.elapsed_time(e1)
             ops += 2 * n * L["K"] * L["N"]
+            abytes += (n + L["N"]) * dp.i8_pitch(L["K"]) + 2 * n * L["N"]
             launches += 1
     avg_ms = gemm_ms / launches
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOP/s",
-            "frac": achieved / I8_PEAK_TOPS, "traffic": None,
+            "frac": achieved / I8_PEAK_TOPS, "traffic": stored_i8_traffic(),
             "kernel": "k_i8_gemm (INT8 MFMA, dequantisation + record-owned FP16 correction)",
-            "algorithmic_ops_per_launch": ops / launches, "avg_ms": avg_ms, "launches": launches}
+            "algorithmic_ops_per_launch": ops / launches, "algorithmic_bytes_per_launch": abytes / launches,
+            "avg_ms": avg_ms, "launches": launches}
 
     # the same kernels on one 7B-shaped frozen projection (4096 -> 4096) over 16 records x 512
     # tokens, where the INT8 product is large enough for the GEMM's MFMA efficiency to show
