@@ -631,26 +631,30 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     p->n_splits_max = ns;
     p->n_splits_dense_max = nsd;
 
-    // workspace layout
+    // workspace layout (every region 256-byte aligned; a total past 2^62 bytes is refused)
     int64_t off = 0;
-    p->status_off = off;
-    off += kAlign;
-    p->parts_off = off;
-    off = align_up(off + p->B * p->parts_total * 4);
-    p->n_off = off;
-    off = align_up(off + p->B * 4);
-    p->c_off = off;
-    off = align_up(off + p->B * 4);
-    p->seg_off = off;
-    if (p->segments) off = align_up(off + (p->B + 1) * 8);
+    bool fits = true;
+    auto region = [&](int64_t count, int64_t elem) -> int64_t {
+        const int64_t at = off;
+        int64_t bytes = 0;
+        if (!mul_ok(count, elem, &bytes) || bytes > ((int64_t)1 << 62) - off) fits = false;
+        else off = align_up(off + bytes);
+        return at;
+    };
+    p->status_off = region(1, kAlign);
+    p->parts_off = region(p->B * p->parts_total, 4);
+    p->n_off = region(p->B, 4);
+    p->c_off = region(p->B, 4);
+    p->seg_off = region(p->segments ? p->B + 1 : 0, 8);
     for (LayerPlan& lp : p->layers) {
-        if (lp.sum_mode == DPSGD_SUM_STORED) {
-            lp.stored_off = off;
-            off = align_up(off + p->B * lp.n_params * 4);
-        } else if ((lp.dense ? nsd : ns) > 1) {
-            lp.split_off = off;
-            off = align_up(off + (int64_t)(lp.dense ? nsd : ns) * lp.n_params * 4);
-        }
+        if (lp.sum_mode == DPSGD_SUM_STORED)
+            lp.stored_off = region(p->B, lp.n_params * 4);
+        else if ((lp.dense ? nsd : ns) > 1)
+            lp.split_off = region(lp.dense ? nsd : ns, lp.n_params * 4);
+    }
+    if (!fits) {
+        delete p;
+        return fail(DPSGD_ERR_INVALID_ARG, "workspace size overflows");
     }
     p->ws_bytes = off;
     *ws_bytes = (size_t)off;
