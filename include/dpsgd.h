@@ -146,7 +146,9 @@ int64_t dpsgd_plan_num_params(const dpsgd_plan* plan);
 /* Segment plans only: set the token-row offsets of the next n_records records
  * in `ws` (host array `offsets` of n_records + 1 entries: offsets[0] = 0,
  * non-decreasing, each segment at most the plan's `tokens` rows; copied
- * stream-ordered, the host array may be reused on return).  The following
+ * stream-ordered: pageable host memory is staged before the call returns and
+ * may be reused at once, pinned host memory must stay unchanged until the
+ * stream has passed the copy).  The following
  * dpsgd_norms / dpsgd_clipped_sum / dpsgd_step calls on this workspace must
  * use the same n_records.  Empty segments are allowed (norm 0, factor 1). */
 int dpsgd_ws_segments(const dpsgd_plan* plan, void* ws, const int64_t* offsets, int64_t n_records,
