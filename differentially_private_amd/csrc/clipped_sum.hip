@@ -12,6 +12,7 @@
 // STORED strategy: the direct norm pass already wrote every record's gradient
 // block; the sum is sum_i c_i P_i over them in ascending record order.
 // Both skip all work while the workspace status reports a nonfinite norm.
+#include "record_sum.h"
 #include "tile_direct.h"
 
 namespace dpsgd {
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(128) void k_sum_direct(DirectArgs args) {
     direct_store<DT, MB>(dst, L, n0, m0, g, c, sum, add);
 }
 
-// out[e] (+)= sum_k w_k src[k][e], k ascending; w_k = clip[k] (STORED) or 1 (split partials).
+// out[e] (+)= sum_k w_k src[k][e], k ascending, accumulated in fp64 and rounded to fp32 once;
+// w_k = clip[k] (STORED) or 1 (split partials).
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     if (a.status && *a.status) return;
@@ -72,30 +74,26 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     if (e >= L.n) return;
     const bool vec = (e + 4 <= L.n) && ((L.n & 3) == 0);
     if (vec) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        double d[4] = {0.0, 0.0, 0.0, 0.0};
         int64_t k = 0;
         for (; k + 8 <= a.n_src; k += 8) {     // 8 independent loads in flight, ascending order
             f32x4 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(L.src + (k + u) * L.n + e);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (WEIGHTED) s += a.clip[k + u] * v[u]; else s += v[u];
-            }
+            for (int u = 0; u < 8; ++u) add_scaled(d, WEIGHTED ? a.clip[k + u] : 1.f, v[u]);
         }
-        for (; k < a.n_src; ++k) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(L.src + k * L.n + e);
-            if (WEIGHTED) s += a.clip[k] * v; else s += v;
-        }
+        for (; k < a.n_src; ++k)
+            add_scaled(d, WEIGHTED ? a.clip[k] : 1.f, *reinterpret_cast<const f32x4*>(L.src + k * L.n + e));
+        f32x4 s = {(float)d[0], (float)d[1], (float)d[2], (float)d[3]};
         if (a.accumulate) s = *reinterpret_cast<const f32x4*>(L.out + e) + s;
         *reinterpret_cast<f32x4*>(L.out + e) = s;
     } else {
         for (int64_t x = e; x < e + 4 && x < L.n; ++x) {
-            float s = 0.f;
-            for (int64_t k = 0; k < a.n_src; ++k) {
-                const float v = L.src[k * L.n + x];
-                if (WEIGHTED) s += a.clip[k] * v; else s += v;
-            }
+            double d = 0.0;
+            for (int64_t k = 0; k < a.n_src; ++k)
+                d = fma(WEIGHTED ? (double)a.clip[k] : 1.0, (double)L.src[k * L.n + x], d);
+            const float s = (float)d;
             L.out[x] = a.accumulate ? L.out[x] + s : s;
         }
     }

@@ -2,6 +2,7 @@
 // gradient blocks (the STORED clipped-sum strategy): in one launch over the
 // flat parameter index e,
 //   out[e] (+)= sum_i c_i P_i[e] + sigma * C * Z[e]
+// (the record sum accumulated in fp64 in ascending i and rounded to fp32 once)
 // ("Privacy-Preserving Machine Learning", DP-SGD phases 3-4: clip each record,
 // sum, add N(0, sigma^2 C^2 I) once), optionally followed by the descent step
 // params[e] -= lr / L * out[e] (phase 5).  When the partials are few, every block
@@ -15,6 +16,7 @@
 #include <atomic>
 
 #include "philox.h"
+#include "record_sum.h"
 
 namespace dpsgd {
 
@@ -107,11 +109,11 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
     }
     if (skip || !active) return;
 
-    // 4) out (+)= sum_i c_i P_i (ascending i) + sigma C Z
+    // 4) out (+)= sum_i c_i P_i (ascending i, accumulated in fp64 and rounded once) + sigma C Z
     if (vec) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        double d[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int u = 0; u < kFinalBatch; ++u) s += keep_or_zero(cf[u < nb0 ? u : 0], u < nb0) * v[u];
+        for (int u = 0; u < kFinalBatch; ++u) add_scaled(d, keep_or_zero(cf[u < nb0 ? u : 0], u < nb0), v[u]);
         for (int64_t i = kFinalBatch; i < a.n_rec; i += 8) {   // further records, 8 loads at a time
             f32x4 w8[8];
 #pragma unroll
@@ -121,8 +123,9 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                s += keep_or_zero(cf[i + u < a.n_rec ? i + u : 0], i + u < a.n_rec) * w8[u];
+                add_scaled(d, keep_or_zero(cf[i + u < a.n_rec ? i + u : 0], i + u < a.n_rec), w8[u]);
         }
+        f32x4 s = {(float)d[0], (float)d[1], (float)d[2], (float)d[3]};
         f32x4* o = reinterpret_cast<f32x4*>(a.out[l] + x0);
         if (a.accumulate) s = *o + s;
         s[0] += a.scale * z[0];
@@ -149,8 +152,9 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
             gauss4(e >> 2, a.step, a.seed, z4);
             z = z4[e & 3];
         }
-        float s = 0.f;
-        for (int64_t i = 0; i < a.n_rec; ++i) s += cf[i] * a.src[l][i * n_l + x];
+        double d = 0.0;
+        for (int64_t i = 0; i < a.n_rec; ++i) d = fma((double)cf[i], (double)a.src[l][i * n_l + x], d);
+        float s = (float)d;
         float* o = a.out[l] + x;
         if (a.accumulate) s = *o + s;
         const float v = s + a.scale * z;

@@ -108,3 +108,35 @@ def test_gram_per_record_sweep(case):
     e = max_rel(got, want)
     say(f"  rel {e:.2e}")
     assert e <= TOL[BF16]
+
+
+# The largest record count a plan accepts (65535), on every path, with tiny layers: one
+# workgroup row per record in the norm launches, clip factors in their own launch, the fused
+# tail's record loop and the GEMM sums' record splits all at their widest.
+MAX_RECORD_CASES = [
+    (F32, dp.PATH_GRAM, dp.SUM_AUTO),
+    (F32, dp.PATH_DIRECT, dp.SUM_STORED),
+    (F32, dp.PATH_DIRECT, dp.SUM_GEMM),
+    (BF16, dp.PATH_DIRECT, dp.SUM_STORED),
+    (BF16, dp.PATH_GRAM, dp.SUM_AUTO),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MAX_RECORD_CASES)))
+def test_maximum_record_count(case):
+    dtype, path, sum_policy = MAX_RECORD_CASES[case]
+    B, T, layers = 65535, 2, ((4, 3), (3, 5))
+    w = datagen.Workload(name=f"maxrec{case}", layers=layers, layer_names=("l0", "l1"), dtype=dtype,
+                         B=B, logical_B=B, T=T, C=1.0, sigma=0.5, data_seed=9100 + case)
+    say("max records", case, "dtype", dtype, "path", path, "sum", sum_policy, "B", B)
+    As, Gs = host_inputs(w)
+    ref = oracle.step(As, Gs, w.C, w.sigma, 5, 2)
+    r = gpu_step(w, As, Gs, DEV, seed=5, step=2, path=path, sum_policy=sum_policy)
+    r0 = gpu_step(w, As, Gs, DEV, seed=5, step=2, path=path, sum_policy=sum_policy, flags=dp.NO_NOISE)
+    tol = TOL[dtype]
+    en, ec = max_rel(r["n"], ref["n"]), max_rel(r["c"], ref["c"])
+    eS = rel_err(flat(r["out"]), flat(ref["S_noised"]))
+    e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
+    say(f"  norm {en:.2e} clip {ec:.2e} noised {eS:.2e} pre-noise {e0:.2e}")
+    assert r["status"] == dp.OK and r0["status"] == dp.OK
+    assert en <= tol and ec <= tol and eS <= tol and e0 <= tol
