@@ -9,6 +9,9 @@
 - The bf16 Gram path for records of at most 256 tokens (one workgroup per record and layer):
   random T, widths (multiples of 32) and record counts; per-layer squared norms against the
   oracle.
+- The largest record count a plan accepts, on every path.
+- The GEMM clipped sums (tile engine with record splits; dense kernels for wide bf16 layers, both
+  the copy kernel and the register kernel) on random plans.
 """
 import numpy as np
 import pytest
@@ -134,6 +137,51 @@ def test_maximum_record_count(case):
     r = gpu_step(w, As, Gs, DEV, seed=5, step=2, path=path, sum_policy=sum_policy)
     r0 = gpu_step(w, As, Gs, DEV, seed=5, step=2, path=path, sum_policy=sum_policy, flags=dp.NO_NOISE)
     tol = TOL[dtype]
+    en, ec = max_rel(r["n"], ref["n"]), max_rel(r["c"], ref["c"])
+    eS = rel_err(flat(r["out"]), flat(ref["S_noised"]))
+    e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
+    say(f"  norm {en:.2e} clip {ec:.2e} noised {eS:.2e} pre-noise {e0:.2e}")
+    assert r["status"] == dp.OK and r0["status"] == dp.OK
+    assert en <= tol and ec <= tol and eS <= tol and e0 <= tol
+
+
+def _gemm_case(i):
+    rng = np.random.default_rng(7200 + i)
+    dtype = F32 if i % 2 == 0 else BF16
+    n_layers = int(rng.integers(1, 4))
+    layers = []
+    for _ in range(n_layers):
+        if rng.random() < 0.5:   # both widths above 16: the dense kernels for bf16
+            layers.append((int(rng.integers(17, 300)), int(rng.integers(17, 300))))
+        else:
+            layers.append((int(rng.integers(1, 120)), int(rng.integers(1, 40))))
+    T = int(32 * rng.integers(1, 4)) if rng.random() < 0.5 else int(rng.integers(1, 97))
+    return dict(dtype=dtype, layers=tuple(layers), B=int(rng.integers(1, 25)), T=T, seed=8200 + i,
+                path=dp.PATH_GRAM if i % 5 == 4 else dp.PATH_DIRECT)
+
+
+GEMM_CASES = [_gemm_case(i) for i in range(14)] + [
+    dict(dtype=BF16, layers=((256, 128), (64, 512)), B=9, T=64, seed=9201, path=dp.PATH_DIRECT),  # copy kernel
+    dict(dtype=BF16, layers=((200, 136),), B=13, T=50, seed=9202, path=dp.PATH_DIRECT),           # register kernel
+]
+
+
+@pytest.mark.parametrize("case", range(len(GEMM_CASES)))
+def test_gemm_sum_sweep(case):
+    """The GEMM clipped sums (the tile engine with its record splits, and for bf16 layers wider than
+    16 in both dimensions the dense kernels) on random plans: norms, factors, pre-noise and noised
+    sums against the oracle."""
+    c = GEMM_CASES[case]
+    w = datagen.Workload(name=f"gsum{case}", layers=c["layers"],
+                         layer_names=tuple(f"l{l}" for l in range(len(c["layers"]))), dtype=c["dtype"],
+                         B=c["B"], logical_B=c["B"], T=c["T"], C=1.0, sigma=0.3, data_seed=c["seed"])
+    say("gemm sweep", case, "dtype", c["dtype"], "path", c["path"], "B", c["B"], "T", c["T"], c["layers"])
+    As, Gs = host_inputs(w)
+    ref = oracle.step(As, Gs, w.C, w.sigma, 4, 9)
+    r = gpu_step(w, As, Gs, DEV, seed=4, step=9, path=c["path"], sum_policy=dp.SUM_GEMM)
+    r0 = gpu_step(w, As, Gs, DEV, seed=4, step=9, path=c["path"], sum_policy=dp.SUM_GEMM,
+                  flags=dp.NO_NOISE)
+    tol = TOL[w.dtype]
     en, ec = max_rel(r["n"], ref["n"]), max_rel(r["c"], ref["c"])
     eS = rel_err(flat(r["out"]), flat(ref["S_noised"]))
     e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
