@@ -297,3 +297,39 @@ def test_max_width():
     A, offsets, _, _ = gen.activations(64, [20, 12], 32768, n_shared=8, p_owned=1.0)
     L = Layer(gen.weights(64, 40, 32768))
     check(A, offsets, L)
+
+
+def _near_half_rows(K):
+    """fp16 rows whose quotients 127 a / s fall on or next to half-integers: exact ties (s = 127/64,
+    a = (k + 1/2)/64, so 127 a / s = k + 1/2) and, for other row maxima s, every fp16 value a in
+    (0, s] whose quotient lies within 1e-3 of a half-integer, with both signs."""
+    rows = []
+    tie = np.array([(k + 0.5) / 64 for k in range(126)], dtype=np.float64)
+    extra = np.random.default_rng(43).uniform(0.05, 5.99, 40)
+    for s in [127 / 64, 1.0, 2.9921875, 5.99609375, 0.3330078125, 4.125, 0.0999755859375, *extra]:
+        s16 = F16(s)
+        grid = np.arange(1, 65536, dtype=np.uint16).view(F16).astype(np.float64)   # all positive fp16
+        grid = grid[np.isfinite(grid) & (grid > 0) & (grid <= float(s16))]
+        q = 127.0 * grid / float(s16)
+        near = grid[np.abs(q - np.floor(q) - 0.5) < 1e-3]
+        vals = np.concatenate([tie if s == 127 / 64 else near, [float(s16)]])
+        vals = np.concatenate([vals, -vals[: len(vals) // 2]])
+        for i in range(0, len(vals), K - 1):
+            chunk = vals[i:i + K - 1]
+            row = np.zeros(K, dtype=np.float64)
+            row[: len(chunk)] = chunk
+            row[-1] = float(s16)          # the row's maximum, below the outlier threshold
+            rows.append(row)
+    return np.array(rows).astype(F16)
+
+
+def test_codes_near_half_integers():
+    """Codes round(127 a / s) where the quotient is a tie or within 1e-3 of one (where the
+    rounding of the division and ties-to-even decide the code): bit-exact with the oracle."""
+    K = 256
+    A = _near_half_rows(K)
+    n = A.shape[0]
+    offsets = [0, n // 3, n]
+    say("int8 near-half codes", n, "rows")
+    L = Layer(gen.weights(41, 64, K))
+    check(A, offsets, L)
