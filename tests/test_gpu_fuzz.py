@@ -1,0 +1,63 @@
+"""Random plans through dpsgd_step against the oracle: 1-5 layers of random widths (narrow,
+LoRA-like and wide), fp32 or bf16, 1-39 records, T of 1-139 tokens or whole 32-token steps, every
+path policy and sum policy, C spanning clipped and unclipped records.  Norms, clip factors, the
+pre-noise sum and the noised sum must meet the fp32 / bf16 bounds.  DPSGD_FUZZ_CASES (default 60)
+and DPSGD_FUZZ_SEED (default 100) set the number of plans and the first seed."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import datagen  # noqa: E402
+import differentially_private_amd as dp  # noqa: E402
+import oracle  # noqa: E402
+from _helpers import TOL, flat, gpu_step, host_inputs, max_rel, rel_err  # noqa: E402
+from datagen import BF16, F32  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+N_CASES = int(os.environ.get("DPSGD_FUZZ_CASES", "60"))
+SEED0 = int(os.environ.get("DPSGD_FUZZ_SEED", "100"))
+
+
+def _plan(i):
+    rng = np.random.default_rng(SEED0 + i)
+    dtype = F32 if rng.random() < 0.5 else BF16
+    layers = []
+    for _ in range(int(rng.integers(1, 6))):
+        r = rng.random()
+        if r < 0.3:
+            layers.append((int(rng.integers(1, 20)), int(rng.integers(1, 20))))
+        elif r < 0.7:
+            layers.append((int(rng.integers(1, 400)), int(rng.integers(1, 24))))
+        else:
+            layers.append((int(rng.integers(17, 260)), int(rng.integers(17, 260))))
+    if rng.random() < 0.25:
+        layers = [(b, a) for a, b in layers]
+    B = int(rng.integers(1, 40))
+    T = int(rng.choice([int(rng.integers(1, 140)), 32 * int(rng.integers(1, 5))]))
+    path = int(rng.choice([dp.PATH_AUTO, dp.PATH_GRAM, dp.PATH_DIRECT]))
+    sum_policy = int(rng.choice([dp.SUM_AUTO, dp.SUM_GEMM, dp.SUM_STORED]))
+    C = float(rng.choice([0.1, 1.0, 50.0]))
+    return dtype, tuple(layers), B, T, path, sum_policy, C
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_plan(i):
+    dtype, layers, B, T, path, sum_policy, C = _plan(i)
+    print("fuzz", SEED0 + i, dtype, path, sum_policy, B, T, C, layers, flush=True)
+    w = datagen.Workload(name=f"fuzz{i}", layers=layers, layer_names=tuple(f"l{l}" for l in range(len(layers))),
+                         dtype=dtype, B=B, logical_B=B, T=T, C=C, sigma=0.4, data_seed=20000 + SEED0 + i)
+    As, Gs = host_inputs(w)
+    ref = oracle.step(As, Gs, w.C, w.sigma, 6, 1)
+    r0 = gpu_step(w, As, Gs, DEV, seed=6, step=1, path=path, sum_policy=sum_policy, flags=dp.NO_NOISE)
+    r = gpu_step(w, As, Gs, DEV, seed=6, step=1, path=path, sum_policy=sum_policy)
+    tol = TOL[dtype]
+    assert r["status"] == dp.OK and r0["status"] == dp.OK
+    assert max_rel(r["n"], ref["n"]) <= tol and max_rel(r["c"], ref["c"]) <= tol
+    assert rel_err(flat(r0["out"]), flat(ref["S"])) <= tol
+    assert rel_err(flat(r["out"]), flat(ref["S_noised"])) <= tol
