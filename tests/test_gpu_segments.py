@@ -4,8 +4,9 @@ records' token rows concatenated) against the oracle.
 The oracle sees the same users as fixed-length records zero-padded to the longest user (zero
 rows add nothing to A^T G), the GPU sees the rows concatenated with an offset array.  Covered:
 the page's Alice/Bao example, random lengths including empty and full segments on the direct
-(STORED and GEMM sum) and Gram paths in fp32 and bf16, and full-length segments giving bitwise
-the fixed-length plan's results on the direct path.
+(STORED and GEMM sum) and Gram paths in fp32 and bf16, 24 random plans (shapes, users, paths and
+sum policies), and full-length segments giving bitwise the fixed-length plan's results on the
+direct path.
 """
 import numpy as np
 import pytest
@@ -75,15 +76,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,layers,dtype,T,path,sum_policy", CASES)
-def test_segments_match_oracle(name, layers, dtype, T, path, sum_policy):
-    B = 7
-    rng = np.random.default_rng(len(name) + T)
-    lens = rng.integers(0, T + 1, B)
-    lens[0], lens[1] = 0, T             # an empty user and a full-length one
-    say("segments", name, "lengths", lens.tolist())
+def _segment_case(name, layers, dtype, T, path, sum_policy, lens, C, sigma, data_seed):
+    """The users of `lens` through a segment plan against the oracle on the same users zero-padded
+    to T rows: norms, factors, noised and pre-noise sums."""
+    B = len(lens)
+    say("segments", name, "dtype", dtype, "path", path, "sum", sum_policy, "T", T, "lengths", list(lens))
     w = datagen.Workload(name=name, layers=layers, layer_names=tuple("l%d" % i for i in range(len(layers))),
-                         dtype=dtype, B=B, logical_B=B, T=T, C=0.7, sigma=0.9, data_seed=700 + T)
+                         dtype=dtype, B=B, logical_B=B, T=T, C=C, sigma=sigma, data_seed=data_seed)
     As, Gs = host_inputs(w)
     # oracle: users as fixed-length records, rows past each user's length zeroed
     zero = np.uint16(0) if dtype == BF16 else np.float32(0)
@@ -103,13 +102,48 @@ def test_segments_match_oracle(name, layers, dtype, T, path, sum_policy):
     en, ec = max_rel(r["n"], ref["n"]), max_rel(r["c"], ref["c"])
     eS = rel_err(flat(r["out"]), flat(ref["S_noised"]))
     say(f"  norm {en:.2e} clip {ec:.2e} noised sum {eS:.2e}")
-    assert r["n"][0] == 0.0 and r["c"][0] == 1.0        # the empty user
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert r["n"][i] == 0.0 and r["c"][i] == 1.0        # an empty user
     assert en <= tol and ec <= tol and eS <= tol
     r0 = run_segments(layers, dtype, T, lens, rows_A, rows_G, w.C, w.sigma, path, sum_policy,
                       flags=dp.NO_NOISE)
     e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
     say(f"  pre-noise sum {e0:.2e}")
     assert e0 <= tol
+
+
+@pytest.mark.parametrize("name,layers,dtype,T,path,sum_policy", CASES)
+def test_segments_match_oracle(name, layers, dtype, T, path, sum_policy):
+    B = 7
+    rng = np.random.default_rng(len(name) + T)
+    lens = rng.integers(0, T + 1, B)
+    lens[0], lens[1] = 0, T             # an empty user and a full-length one
+    _segment_case(name, layers, dtype, T, path, sum_policy, lens, 0.7, 0.9, 700 + T)
+
+
+def _random_segment_case(i):
+    rng = np.random.default_rng(6100 + i)
+    dtype = F32 if i % 2 == 0 else BF16
+    layers = tuple((int(rng.integers(1, 200)), int(rng.integers(1, 40))) if rng.random() < 0.6
+                   else (int(rng.integers(17, 200)), int(rng.integers(17, 200)))
+                   for _ in range(int(rng.integers(1, 4))))
+    T = int(rng.integers(1, 130))
+    B = int(rng.integers(1, 25))
+    lens = rng.integers(0, T + 1, B)
+    if B > 2 and rng.random() < 0.5:
+        lens[rng.integers(0, B)] = 0
+    path = int(rng.choice([dp.PATH_AUTO, dp.PATH_GRAM, dp.PATH_DIRECT]))
+    sum_policy = int(rng.choice([dp.SUM_AUTO, dp.SUM_GEMM, dp.SUM_STORED]))
+    return dict(name=f"rseg{i}", layers=layers, dtype=dtype, T=T, path=path, sum_policy=sum_policy,
+                lens=lens, C=float(rng.choice([0.2, 1.0, 30.0])), sigma=0.6, data_seed=6200 + i)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_segment_plans(i):
+    """Random segment plans: 1-3 layers (LoRA-like or wide), fp32 and bf16, 1-24 users of 0-T rows,
+    every path and sum policy."""
+    _segment_case(**_random_segment_case(i))
 
 
 def test_full_length_segments_equal_fixed_records():
