@@ -333,3 +333,26 @@ def test_codes_near_half_integers():
     say("int8 near-half codes", n, "rows")
     L = Layer(gen.weights(41, 64, K))
     check(A, offsets, L)
+
+
+def _random_forward(i):
+    rng = np.random.default_rng(90000 + i)
+    K = int(rng.choice([int(rng.integers(1, 600)), 32 * int(rng.integers(1, 40))]))
+    N = int(rng.integers(1, 700))
+    lens = [int(x) for x in rng.integers(0, 90, int(rng.integers(1, 30)))]
+    if sum(lens) == 0:
+        lens[0] = 1
+    tau = float(rng.choice([6.0, 3.0, 1.5, 0.0]))
+    one_record = rng.random() >= 0.8
+    return K, N, lens, tau, one_record, int(rng.integers(0, 5)), float(rng.random())
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_forwards(i):
+    """Random layers (K of 1-599 or whole 32-column groups, 1-699 features), 1-29 records of
+    0-89 rows, thresholds 0-6, record-owned or one record over the batch: bit-exact."""
+    K, N, lens, tau, one_record, n_shared, p_owned = _random_forward(i)
+    say("int8 random", i, "K", K, "N", N, "records", len(lens), "tau", tau, "one record", one_record)
+    A, offsets, _, _ = gen.activations(i, lens, K, tau=max(tau, 1.0), n_shared=n_shared, p_owned=p_owned)
+    L = Layer(gen.weights(i, N, K))
+    check(A, [0, int(offsets[-1])] if one_record else offsets, L, tau=tau)
