@@ -2,7 +2,8 @@
 LoRA-like and wide), fp32 or bf16, 1-39 records, T of 1-139 tokens or whole 32-token steps, every
 path policy and sum policy, C spanning clipped and unclipped records.  Norms, clip factors, the
 pre-noise sum and the noised sum must meet the fp32 / bf16 bounds.  DPSGD_FUZZ_CASES (default 60)
-and DPSGD_FUZZ_SEED (default 100) set the number of plans and the first seed."""
+and DPSGD_FUZZ_SEED (default 100) set the number of plans and the first seed.  Twelve more plans
+run as virtual batches (2-5 physical batches, the last one shorter, noise once)."""
 import os
 
 import numpy as np
@@ -15,7 +16,7 @@ if not torch.cuda.is_available():
 import datagen  # noqa: E402
 import differentially_private_amd as dp  # noqa: E402
 import oracle  # noqa: E402
-from _helpers import TOL, flat, gpu_step, host_inputs, max_rel, rel_err  # noqa: E402
+from _helpers import TOL, flat, gpu_step, host_inputs, max_rel, rel_err, to_device  # noqa: E402
 from datagen import BF16, F32  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -61,3 +62,42 @@ def test_random_plan(i):
     assert max_rel(r["n"], ref["n"]) <= tol and max_rel(r["c"], ref["c"]) <= tol
     assert rel_err(flat(r0["out"]), flat(ref["S"])) <= tol
     assert rel_err(flat(r["out"]), flat(ref["S_noised"])) <= tol
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_virtual_batches(i):
+    """A random plan run as 2-5 physical batches (the last one shorter) accumulated into one
+    output, noise drawn once at the end: equal to the oracle's logical step."""
+    dtype, layers, B, T, path, sum_policy, C = _plan(1000 + i)
+    rng = np.random.default_rng(SEED0 + 5000 + i)
+    n_phys = int(rng.integers(2, 6))
+    last = int(rng.integers(1, B + 1))
+    sizes = [B] * (n_phys - 1) + [last]
+    print("virtual", dtype, path, sum_policy, B, T, C, layers, sizes, flush=True)
+    w = datagen.Workload(name=f"vfuzz{i}", layers=layers, layer_names=tuple(f"l{l}" for l in range(len(layers))),
+                         dtype=dtype, B=B, logical_B=sum(sizes), T=T, C=C, sigma=0.4,
+                         data_seed=40000 + SEED0 + i)
+    plan = dp.Plan(layers, dtype, B, T, path, sum_policy)
+    ws = plan.workspace(DEV)
+    out = [torch.empty(a * b, dtype=torch.float32, device=DEV) for a, b in layers]
+    batches, ns, cs, first = [], [], [], 0
+    for p, nb in enumerate(sizes):
+        As, Gs = host_inputs(w, first=first, n=nb)
+        first += nb
+        batches.append((As, Gs))
+        nrm = torch.empty(B, dtype=torch.float32, device=DEV)
+        cf = torch.empty(B, dtype=torch.float32, device=DEV)
+        flags = dp.NO_NOISE | (dp.ACCUMULATE if p else 0)
+        dp.step(plan, [to_device(a, DEV) for a in As], [to_device(g, DEV) for g in Gs], out, ws, C,
+                w.sigma, 2, 5, n_records=nb, flags=flags, norms_out=nrm, clip_out=cf)
+        ns.append(nrm.cpu().numpy()[:nb])
+        cs.append(cf.cpu().numpy()[:nb])
+    pre = flat([o.cpu().numpy() for o in out])
+    dp.noise(plan, out, C, w.sigma, 2, 5, ws=ws)
+    assert dp.status(plan, ws) == dp.OK
+    ref = oracle.step(None, None, C, w.sigma, 2, 5, batches=batches)
+    tol = TOL[dtype]
+    assert max_rel(np.concatenate(ns), ref["n"]) <= tol
+    assert max_rel(np.concatenate(cs), ref["c"]) <= tol
+    assert rel_err(pre, flat(ref["S"])) <= tol
+    assert rel_err(flat([o.cpu().numpy() for o in out]), flat(ref["S_noised"])) <= tol
