@@ -26,9 +26,8 @@ __global__ __launch_bounds__(1024) void k_clip(ClipArgs a) {
         const int64_t rec = rec0 + (int64_t)lane * nw;
         if (lane < 4 && rec < a.n_rec) {
             const double s = lane == 0 ? s4[0] : lane == 1 ? s4[1] : lane == 2 ? s4[2] : s4[3];
-            const double n = sqrt(s);
-            const double cf = (n <= a.C) ? 1.0 : a.C / n;
-            if (!isfinite(s)) atomicOr(&bad, 1u);
+            double n, cf;
+            if (clip_of_norm2(s, a.C, n, cf)) atomicOr(&bad, 1u);
             a.n_ws[rec] = (float)n;
             a.c_ws[rec] = (float)cf;
             if (a.n_user) a.n_user[rec] = (float)n;
@@ -51,7 +50,7 @@ __global__ __launch_bounds__(256) void k_layer_norm2(LayerNormArgs a) {
     const float* p = a.parts + rec * a.parts_stride + a.part_off[l];
     double s = 0.0;
     for (int k = 0; k < a.n_part[l]; ++k) s += (double)p[k];
-    a.out[idx] = (float)s;
+    a.out[idx] = (float)(s < 0.0 ? 0.0 : s);   // a squared norm: a negative rounded sum is 0
 }
 
 hipError_t launch_clip(const ClipArgs& a, hipStream_t s) {

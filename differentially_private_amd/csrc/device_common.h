@@ -115,6 +115,20 @@ __device__ __forceinline__ void record_norm2_x4(const float* __restrict__ parts,
     record_norm2_x4_from(v0, parts, stride, n_parts, rec0, rec_step, n_rec, lane, out);
 }
 
+// Norm and clip factor of one record from the sum s of its partial squared norms
+// ("Privacy-Preserving Machine Learning", DP-SGD phase 3: n = ||g||, c = min(1, C/n), a
+// zero gradient left unchanged).  s is a sum of squares, but the Gram path's partials of
+// off-diagonal token blocks are signed, and for a record whose token contributions nearly
+// cancel their rounded sum can fall below zero: a negative s is taken as 0 (n = 0, c = 1).
+// A NaN s stays NaN in n and c.  Returns true when s, or n or c as stored in fp32, is not
+// finite (the caller raises the nonfinite status).
+__device__ __forceinline__ bool clip_of_norm2(double s, double C, double& n, double& c) {
+    const double s0 = s < 0.0 ? 0.0 : s + 0.0;   // + 0.0 turns a -0 into +0
+    n = sqrt(s0);
+    c = (n <= C) ? 1.0 : C / n;
+    return !isfinite(s) || !isfinite((float)n) || !isfinite((float)c);
+}
+
 // LDS byte address of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;

@@ -88,9 +88,8 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
             const int64_t rec = rec0 + (int64_t)lane * nw;
             if (lane < 4 && rec < a.n_rec) {
                 const double s = lane == 0 ? s4[0] : lane == 1 ? s4[1] : lane == 2 ? s4[2] : s4[3];
-                const double n = sqrt(s);
-                const double c = (n <= a.C) ? 1.0 : a.C / n;
-                if (!isfinite(s)) atomicOr(&bad, 1u);
+                double n, c;
+                if (clip_of_norm2(s, a.C, n, c)) atomicOr(&bad, 1u);
                 cs[rec] = (float)c;
                 if (blockIdx.x == 0 && l == 0) {
                     a.n_ws[rec] = (float)n;

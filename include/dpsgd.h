@@ -170,8 +170,11 @@ int dpsgd_norms(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int32_t l
 
 /* Phase 2 (DP-SGD phase 3, g * min(1, C/||g||)): n_i and c_i from the partials
  * of all layers (fixed summation order: record i's results do not depend on the
- * other records, their number or i's position).  Sets the status word to
- * NONFINITE if some n_i is NaN/Inf (ORs into it with DPSGD_ACCUMULATE).
+ * other records, their number or i's position).  n_i^2 is the sum of the
+ * partials, taken as 0 when rounding makes it negative (Gram-path records whose
+ * token contributions nearly cancel), so n_i >= 0 and c_i is in (0, 1].  Sets
+ * the status word to NONFINITE if some n_i^2, n_i or c_i is NaN/Inf (ORs into
+ * it with DPSGD_ACCUMULATE).
  * norms_out / clip_out are optional device arrays of n_records floats. */
 int dpsgd_clip(const dpsgd_plan* plan, int64_t n_records, double C, uint32_t flags, void* ws,
                float* norms_out, float* clip_out, void* stream);
@@ -335,7 +338,9 @@ int dpsgd_i8_intermediates(const dpsgd_i8_plan* plan, const void* ws, int64_t n_
 int dpsgd_status(const dpsgd_plan* plan, const void* ws, void* stream);
 
 /* Per-layer squared norms of layers [l0, l1) from the partials of the last
- * dpsgd_norms: out[(l - l0) * n_records + i] = ||P_{i,l}||_F^2 (device). */
+ * dpsgd_norms: out[(l - l0) * n_records + i] = ||P_{i,l}||_F^2 (device).  On the
+ * Gram path the partials of off-diagonal token blocks are signed; a negative
+ * rounded sum is reported as 0. */
 int dpsgd_layer_norm2(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int32_t l1,
                       const void* ws, float* out, void* stream);
 
