@@ -135,6 +135,15 @@ int check_c_sigma(double C, double sigma, bool need_sigma) {
 
 // ---- phase implementations (arguments already validated) ----
 
+// Layers per launch when `count` layers go out in launches of at most `cap`: as few launches as
+// the cap allows, with their layer counts as equal as possible (so that every launch of a phase
+// moves about the same bytes and a per-launch average describes each of them).
+int balanced_chunk(int count, int cap) {
+    if (count <= 0) return cap;
+    const int launches = (count + cap - 1) / cap;
+    return (count + launches - 1) / launches;
+}
+
 // Waves per workgroup for a launch group: 2 when every layer's column-tile count
 // is even, else 1, so that no workgroup carries idle waves (measured on the
 // LoRA workloads: small workgroups stream best; 4-8 waves per workgroup were
@@ -155,6 +164,13 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
     // direct layers, grouped by (MB, store); Gram layers in their own launches
     for (int mb = 1; mb <= 2; ++mb) {
         for (int store = 0; store <= 1; ++store) {
+            auto in_group = [&](const LayerPlan& lp) {
+                return lp.path == DPSGD_PATH_DIRECT && lp.tiles.mb == mb &&
+                       (lp.sum_mode == DPSGD_SUM_STORED) == (store == 1);
+            };
+            int count = 0;
+            for (int l = l0; l < l1; ++l) count += in_group(p->layers[l]) ? 1 : 0;
+            const int per = balanced_chunk(count, kMaxLaunchLayers);
             DirectArgs a;
             std::memset(&a, 0, sizeof(a));
             a.T = p->T;
@@ -164,9 +180,7 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
             a.seg = ws_seg(ws, p);
             for (int l = l0; l < l1; ++l) {
                 const LayerPlan& lp = p->layers[l];
-                if (lp.path != DPSGD_PATH_DIRECT || lp.tiles.mb != mb ||
-                    (lp.sum_mode == DPSGD_SUM_STORED) != (store == 1))
-                    continue;
+                if (!in_group(lp)) continue;
                 DirectLayer& d = a.L[a.n_layers];
                 const void* a_ptr = A[l - l0];
                 const void* g_ptr = G[l - l0];
@@ -183,7 +197,7 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
                 d.vec_x = ptr_aligned16(d.X) && ((lp.tiles.dX * es) % 16 == 0);
                 d.d_out = lp.d_out;
                 d.split_stride = 0;
-                if (++a.n_layers == kMaxLaunchLayers) {
+                if (++a.n_layers == per) {
                     set_wpb(a);
                     hipError_t e = launch_norm_direct(a, p->dtype, mb, store != 0, s);
                     if (e != hipSuccess) return hip_fail(e, "ghost_norm (direct) launch");
@@ -399,6 +413,12 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
             r.max_n4 = 0;
             return DPSGD_OK;
         };
+        int count = 0;
+        for (int l = l0; l < l1; ++l) {
+            const LayerPlan& lp = p->layers[l];
+            count += (lp.sum_mode == DPSGD_SUM_GEMM && !lp.dense && lp.tiles.mb == mb) ? 1 : 0;
+        }
+        const int per = balanced_chunk(count, kMaxLaunchLayers);
         for (int l = l0; l < l1; ++l) {
             const LayerPlan& lp = p->layers[l];
             if (lp.sum_mode != DPSGD_SUM_GEMM || lp.dense || lp.tiles.mb != mb) continue;
@@ -427,7 +447,7 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
                 d.P = out[l - l0];
                 d.split_stride = 0;
             }
-            if (++a.n_layers == kMaxLaunchLayers) {
+            if (++a.n_layers == per) {
                 int rc = flush();
                 if (rc) return rc;
             }
@@ -442,9 +462,10 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
 int do_noise(const dpsgd_plan* p, float* const* out, float* const* params, double descent, double C,
              double sigma, uint64_t seed, uint64_t step, const void* ws, hipStream_t s) {
     const int L = (int)p->layers.size();
+    const int per = balanced_chunk(L, kNoiseMaxLayers);
     NoiseArgs a;
-    for (int l0 = 0; l0 < L; l0 += kNoiseMaxLayers) {
-        const int l1 = std::min(L, l0 + kNoiseMaxLayers);
+    for (int l0 = 0; l0 < L; l0 += per) {
+        const int l1 = std::min(L, l0 + per);
         std::memset(&a, 0, sizeof(a));
         a.n_layers = l1 - l0;
         a.seed = seed;
@@ -474,9 +495,10 @@ int do_finalize(const dpsgd_plan* p, int64_t n_rec, double C, double sigma, uint
     if (!inside)
         if (int rc = do_clip(p, n_rec, C, flags, ws, n_user, c_user, s)) return rc;
     const int L = (int)p->layers.size();
+    const int per = balanced_chunk(L, kFinalMaxLayers);
     FinalizeArgs a;
-    for (int l0 = 0; l0 < L; l0 += kFinalMaxLayers) {
-        const int l1 = std::min(L, l0 + kFinalMaxLayers);
+    for (int l0 = 0; l0 < L; l0 += per) {
+        const int l1 = std::min(L, l0 + per);
         std::memset(&a, 0, sizeof(a));
         a.n_layers = l1 - l0;
         a.accumulate = (flags & DPSGD_ACCUMULATE) ? 1 : 0;

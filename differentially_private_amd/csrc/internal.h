@@ -9,7 +9,7 @@
 namespace dpsgd {
 
 constexpr int kMaxLaunchLayers = 48;  // per-launch layer descriptors (kernarg <= 4 KB)
-constexpr int kNoiseMaxLayers = 64;
+constexpr int kNoiseMaxLayers = 128;  // NoiseArgs stays under 4 KB (checked below)
 
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
@@ -110,6 +110,7 @@ struct NoiseArgs {
     const uint32_t* status;
     float* params[kNoiseMaxLayers];    // descent step targets, or all null
 };
+static_assert(sizeof(NoiseArgs) <= 4096, "kernel arguments of the noise launch exceed 4 KB");
 
 constexpr int kFinalMaxLayers = 48;
 constexpr int kFinalMaxRecords = 1024;      // records whose factors a block recomputes itself
@@ -181,6 +182,11 @@ struct LayerNormArgs {
     int32_t n_part[kMaxLaunchLayers];
     float* out;
 };
+
+static_assert(sizeof(DirectArgs) <= 4096 && sizeof(GramArgs) <= 4096 && sizeof(ReduceArgs) <= 4096 &&
+                  sizeof(FinalizeArgs) <= 4096 && sizeof(DenseSumArgs) <= 4096 &&
+                  sizeof(LayerNormArgs) <= 4096,
+              "kernel arguments travel by value and must stay under 4 KB");
 
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s);

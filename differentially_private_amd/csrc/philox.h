@@ -25,10 +25,12 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint64_t block, uint64_t step, 
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * x0;
-        const uint32_t hi0 = __umulhi(0xD2511F53u, x0);
-        const uint32_t lo1 = 0xCD9E8D57u * x2;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2);
+        // each 32 x 32 -> 64-bit product as one 64-bit multiply, so that both halves come
+        // from a single v_mad_u64_u32 rather than a mul_lo / mul_hi pair
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         const uint32_t y0 = hi1 ^ x1 ^ k0;
         const uint32_t y2 = hi0 ^ x3 ^ k1;
         x0 = y0;
