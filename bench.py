@@ -2,19 +2,25 @@
 """Benchmark of the DP-SGD private-gradient step (ghost per-record norms -> clip -> clipped sum ->
 Gaussian noise) on one MI355X, through the library's C ABI.
 
-Default workload: the OPT-125M-shaped rank-8 LoRA on q,v of 12 blocks (48 linear layers,
-294,912 trainables), 16 records x 128 tokens, fp32 activations and output gradients ~ N(0,1),
-C = 1, sigma = 1.  Inputs are synthetic (the seeded generator, written straight into HBM) and
-resident before timing.  A step is one pass of the whole path over one batch.
+Default workload (the largest configuration that fits one GPU): the 7B-shaped rank-16 LoRA on
+q, k, v, o of 32 blocks (256 linear layers, 16.8M trainables), 256 records x 512 tokens, bf16
+activations and output gradients ~ N(0, 0.02) with Student-t(3) records 0, 100, 200, C = 0.5,
+sigma = 0.8: 276 GB of inputs, all resident in HBM before timing.  --workload N (1-5) runs the
+other configurations; --sum gemm replaces the default clipped-sum strategy (per-record gradient
+blocks kept by the norm pass where that moves fewer bytes) by the GEMM A^T diag(c) G that
+re-reads A and G.  Inputs are synthetic (the seeded generator, written straight into HBM).  A step
+is one pass of the whole path over one logical batch (every physical batch, the noise once).
 
 Prints one JSON line: records/s over --steps timed steps, the roofline of the dominant kernel
-(its average duration from HIP events recorded around it inside the timed loop), and the CPU
-oracle timed on the host's cores on a bounded sample of the same workload.
+(its average duration from HIP events recorded around back-to-back launches of it on the stream
+it runs on), every phase's rate, and the CPU oracle timed on the host's cores on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import subprocess
@@ -28,6 +34,11 @@ METRIC = "records/sec per DP-SGD clip+noise step; % MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0
 DESCENT_LR, DESCENT_L = 0.01, 1.0   # --descent: the sensitivity paper's release audit settings
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0}   # dense fp32 / bf16 MFMA
+DEFAULT_WORKLOAD = 3
+N_SETS = 4   # distinct input batches a single-batch workload's timed steps cycle through
+MAX_LAUNCH_LAYERS = 48   # layers per launch of the norm and tile-engine sum kernels (library)
+SUM_POLICIES = {"auto": 0, "gemm": 1, "stored": 2}
+SUM_NAMES = {0: "auto", 1: "gemm", 2: "stored"}
 
 
 def log(*a):
@@ -35,26 +46,40 @@ def log(*a):
 
 
 def algorithmic_work(w, plan, dp):
-    """Per-phase algorithmic HBM bytes / flops for one physical batch of w."""
+    """Algorithmic HBM bytes and flops of each phase for one physical batch of w: what the method
+    must move or compute.  norms: one read of every A and G (the per-record gradients the ghost
+    norms avoid are not counted); clipped_sum of the GEMM layers: one read of their A and G and the
+    fp32 output; noise: read and write of every parameter (8 bytes).  The per-record gradient
+    blocks that the STORED strategy writes during the norms and reads back in the sum are an
+    implementation choice, reported apart ("stored_write" / "stored_read")."""
     e = 4 if w.dtype == 0 else 2
     B, T = w.B, w.T
-    norm_bytes = norm_flops = sum_bytes = sum_flops = 0
+    work = {"norms": [0, 0], "clipped_sum": [0, 0], "noise": [8 * w.n_params, 0],
+            "stored_write": 0, "stored_read": 0}
     for l, (di, do) in enumerate(w.layers):
         path, sm = plan.layer_info(l)
         in_bytes = B * T * (di + do) * e
-        norm_bytes += in_bytes
-        if path == dp.PATH_GRAM:
-            norm_flops += 2 * B * T * T * (di + do)
-        else:
-            norm_flops += 2 * B * T * di * do
+        work["norms"][0] += in_bytes
+        work["norms"][1] += 2 * B * T * T * (di + do) if path == dp.PATH_GRAM else 2 * B * T * di * do
         if sm == dp.SUM_STORED:
-            norm_bytes += B * di * do * 4            # the per-record gradient blocks written once
-            sum_bytes += B * di * do * 4 + di * do * 4
+            work["stored_write"] += B * di * do * 4
+            work["stored_read"] += B * di * do * 4
         else:
-            sum_bytes += in_bytes + di * do * 4
-            sum_flops += 2 * B * T * di * do
-    return {"norms": (norm_bytes, norm_flops), "clipped_sum": (sum_bytes, sum_flops),
-            "noise": (8 * w.n_params, 0)}
+            work["clipped_sum"][0] += in_bytes + di * do * 4
+            work["clipped_sum"][1] += 2 * B * T * di * do
+    return work
+
+
+def norm_launches(w, plan, dp):
+    """Launches of the norm kernels per physical batch: direct-path layers go out in groups of
+    equal MFMA row blocks and strategy, Gram-path layers in their own, at most 48 layers a launch
+    (the library's kernel-argument limit), split into near-equal launches."""
+    groups = {}
+    for l, (di, do) in enumerate(w.layers):
+        path, sm = plan.layer_info(l)
+        key = ("gram",) if path == dp.PATH_GRAM else ("direct", min(di, do) <= 16, sm)
+        groups[key] = groups.get(key, 0) + 1
+    return sum(-(-n // MAX_LAUNCH_LAYERS) for n in groups.values())
 
 
 def device_inputs(w, datagen, torch, dev, first, n):
@@ -78,10 +103,12 @@ def device_inputs(w, datagen, torch, dev, first, n):
 # sources the ghost-norm kernels are compiled from: a stored HBM-traffic record applies only while
 # these are unchanged
 NORM_KERNEL_SOURCES = ("ghost_norm.hip", "tile_direct.h", "device_common.h", "internal.h")
-
-
-# sources the INT8 forward's kernels are compiled from (same rule for its traffic record)
+# the same for the clipped-sum kernels (tile engine, dense MFMA kernels, split reduce)
+SUM_KERNEL_SOURCES = ("clipped_sum.hip", "clipped_sum_dense.hip", "tile_direct.h", "device_common.h",
+                      "internal.h")
+# the same for the INT8 forward's kernels
 I8_KERNEL_SOURCES = ("int8_forward.hip", "int8.h", "device_common.h", "internal.h")
+PHASE_SOURCES = {"norms": NORM_KERNEL_SOURCES, "clipped_sum": SUM_KERNEL_SOURCES}
 
 
 def kernel_src_hash(names=NORM_KERNEL_SOURCES) -> str:
@@ -91,6 +118,23 @@ def kernel_src_hash(names=NORM_KERNEL_SOURCES) -> str:
         with open(os.path.join(ROOT, "differentially_private_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def traffic_record_path(workload_name, phase, sum_name):
+    return os.path.join(ROOT, "profiles", f"traffic_{phase}_{workload_name}_{sum_name}.json")
+
+
+def stored_traffic(workload_name, phase, sum_name):
+    """HBM-side bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (each scaled by what the same counter reads for a plain copy of known size); None when no
+    record exists or the kernel sources differ from the ones it was measured on."""
+    path = traffic_record_path(workload_name, phase, sum_name)
+    if not os.path.exists(path):
+        return None
+    tr = json.load(open(path))
+    if tr.get("src_hash") != kernel_src_hash(PHASE_SOURCES[phase]):
+        return None
+    return tr.get("bytes_per_launch")
 
 
 def stored_i8_traffic():
@@ -105,52 +149,349 @@ def stored_i8_traffic():
 
 
 def cpu_baseline(w, seconds):
-    import numpy as np  # noqa: F401
+    """The oracle as it stands (plain C, fp64, OpenMP over gradient rows), timed on the host's
+    threads on a bounded sample of the workload: whole steps when one takes well under `seconds`,
+    else the first m records of the logical batch over every layer (m from a one-record probe, so
+    that the timed run takes about `seconds`), the step's noise over every parameter included.
+    Input generation is excluded.  A one-thread figure follows on a shorter sample."""
     import datagen
     import oracle
-    As = [datagen.host_tensor(w, l, 0) for l in range(w.n_layers)]
-    Gs = [datagen.host_tensor(w, l, 1) for l in range(w.n_layers)]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.step(As, Gs, w.C, w.sigma, w.noise_seed, 0)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
     cores = oracle.num_threads()
-    # the same oracle on one thread, on a shorter sample (at least one step)
-    oracle.set_num_threads(1)
-    reps1 = 0
-    t0 = time.perf_counter()
-    try:
+
+    def inputs(m, layers):
+        return ([datagen.host_tensor(w, l, 0, 0, m) for l in layers],
+                [datagen.host_tensor(w, l, 1, 0, m) for l in layers])
+
+    def timed(As, Gs, budget):
+        reps, t0 = 0, time.perf_counter()
         while True:
             oracle.step(As, Gs, w.C, w.sigma, w.noise_seed, 0)
-            reps1 += 1
-            el1 = time.perf_counter() - t0
-            if el1 >= seconds / 3:
-                break
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    layers = range(w.n_layers)
+    As, Gs = inputs(1, layers)
+    t0 = time.perf_counter()
+    oracle.step(As, Gs, w.C, w.sigma, w.noise_seed, 0)
+    t1 = time.perf_counter() - t0
+    n_all = min(w.B, w.logical_B)
+    if t1 * n_all <= seconds / 4:
+        m = n_all                    # whole (physical) batches, repeated
+    else:
+        m = max(1, min(n_all, int(seconds / t1)))
+    if m > 1:
+        As, Gs = inputs(m, layers)
+    reps, el = timed(As, Gs, seconds if m == n_all else 0.0)
+    value = m * reps / el
+    sample = (f"{reps} x {m} records ({'the whole batch' if m == n_all else 'the first of the batch'}) "
+              f"over all {w.n_layers} layers: norms, clip, clipped sum, noise over all {w.n_params} "
+              f"parameters; input generation excluded; {el:.1f} s wall")
+    # one thread: one record, over every k-th layer when a whole record would take long; the rate
+    # is scaled by the share of the per-record work the sampled layers hold
+    oracle.set_num_threads(1)
+    try:
+        per_layer = [2 * w.T * di * do for di, do in w.layers]
+        est1 = t1 * cores
+        k = max(1, int(math.ceil(est1 / (seconds / 3))))
+        sub = list(range(0, w.n_layers, k))
+        share = sum(per_layer[l] for l in sub) / sum(per_layer)
+        As1, Gs1 = inputs(1, sub)
+        reps1, el1 = timed(As1, Gs1, seconds / 3 if k == 1 else 0.0)
+        single = {"value": share * reps1 / el1, "unit": "records/s", "cores": 1,
+                  "sample": f"{reps1} x 1 record over {len(sub)} of {w.n_layers} layers "
+                            f"({share:.3f} of a record's work; the rate is scaled by it), "
+                            f"{el1:.1f} s wall"}
     finally:
         oracle.set_num_threads(cores)
-    return {"value": w.B * reps / el, "unit": "records/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{reps} full steps of the workload ({w.B} records x {w.n_layers} layers, "
-                      f"noise included, input generation excluded), {el:.1f} s wall",
-            "single_thread": {"value": w.B * reps1 / el1, "unit": "records/s", "cores": 1,
-                              "sample": f"{reps1} full steps, {el1:.1f} s wall"}}
+    return {"value": value, "unit": "records/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "single_thread": single}
 
 
-def sum_roofline(work, w, phase):
-    """Algorithmic rate of the clipped-sum phase when it was timed alone (GEMM strategy: flops
-    against the bf16/fp32 MFMA peak; STORED: bytes against HBM)."""
-    if "clipped_sum" not in phase:
+def phase_roofline(phase, nbytes, nflops, ms, dtype):
+    """Rate of one phase against the roofline that binds it: MFMA (the dtype's dense peak) when its
+    arithmetic intensity is above the ridge, else HBM."""
+    if ms <= 0:
         return None
-    sb, sf = work["clipped_sum"]
-    t = phase["clipped_sum"] * 1e-3
-    if sf:
-        peak = MFMA_PEAK_TFLOPS[w.dtype]
-        return {"TFLOPs": sf * w.n_phys / t / 1e12, "mfma_frac": sf * w.n_phys / t / 1e12 / peak}
-    return {"hbm_GBps": sb * w.n_phys / t / 1e9, "hbm_frac": sb * w.n_phys / t / 1e9 / HBM_PEAK_GBS}
+    s = ms * 1e-3
+    mfma_peak = MFMA_PEAK_TFLOPS[dtype]
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    r = {"ms": ms, "algorithmic_bytes": nbytes, "flops": nflops,
+         "GBps": nbytes / s / 1e9, "hbm_frac": nbytes / s / 1e9 / HBM_PEAK_GBS}
+    if nflops:
+        r["TFLOPs"] = nflops / s / 1e12
+        r["mfma_frac"] = r["TFLOPs"] / mfma_peak
+    r["bound"] = "mfma" if nflops and nflops / max(nbytes, 1) > ridge else "hbm"
+    return r
+
+
+KERNEL_NAMES = {
+    "norms": {"direct": "k_norm_direct (ghost_norm, direct path)",
+              "gram": "k_norm_gram_rec / k_norm_gram (ghost_norm, Gram path)"},
+    "clipped_sum": {"dense": "k_sum_dense_dma (clipped_sum, dense MFMA GEMM A^T diag(c) G)",
+                    "tile": "k_sum_direct (clipped_sum, GEMM A^T diag(c) G on the tile engine) + split reduce"},
+}
+
+
+def kernel_name(phase, w, plan, dp):
+    paths = {plan.layer_info(l)[0] for l in range(w.n_layers)}
+    if phase == "norms":
+        return KERNEL_NAMES["norms"]["gram" if paths == {dp.PATH_GRAM} else "direct"]
+    dense = w.dtype == 1 and all(min(di, do) > 16 for di, do in w.layers)
+    return KERNEL_NAMES["clipped_sum"]["dense" if dense else "tile"]
+
+
+def step_line(args, w, torch, dev, dp, datagen):
+    """One JSON line for workload w: whole logical steps timed between HIP events (inputs resident
+    in HBM; single-batch workloads that fit four times cycle through four distinct batches so that
+    no step re-reads inputs the last-level cache kept), then every phase alone, K back-to-back
+    launches between two HIP events on the stream they run on, with the C calls' arguments
+    marshalled once so that the host does not pace the GPU."""
+    import ctypes
+    import numpy as np
+    L = w.n_layers
+    sum_policy = SUM_POLICIES[args.sum]
+    plan = dp.Plan(w.layers, w.dtype, w.B, w.T, dp.PATH_AUTO, sum_policy)
+    ws = plan.workspace(dev)
+    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+    theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+             if args.descent else None)
+    in_bytes = w.input_bytes_per_batch()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    log(f"{w.name}: filling {w.n_phys} physical batch(es) of {in_bytes / 1e9:.2f} GB in HBM")
+    batches = [device_inputs(w, datagen, torch, dev, p * w.B, w.B) for p in range(w.n_phys)]
+    cycle = [batches]
+    free = torch.cuda.mem_get_info()[0]
+    if w.n_phys == 1 and N_SETS * in_bytes < free // 2:
+        cycle += [[device_inputs(w, datagen, torch, dev, k * w.B, w.B)] for k in range(1, N_SETS)]
+    n_cycle = len(cycle)
+    lib = dp.load()
+
+    # whole logical steps: the physical batches with NO_NOISE (ACCUMULATE after the first), then
+    # the noise once; a single physical batch is one dpsgd_step
+    calls = []
+    for bs in cycle:
+        cs = []
+        for p, (As, Gs) in enumerate(bs):
+            flags = (dp.NO_NOISE if w.n_phys > 1 else 0) | (dp.ACCUMULATE if p else 0)
+            last = w.n_phys == 1
+            cs.append(dp.StepCall(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, flags=flags,
+                                  params=theta if last else None, lr=DESCENT_LR, normalizer=DESCENT_L))
+        calls.append(cs)
+    arr_o = dp._ptr_array(out)
+    arr_t = dp._ptr_array(theta)
+    wsp = ws.data_ptr()
+    descent = args.descent
+
+    def noise_call():
+        if descent:
+            rc = lib.dpsgd_noise_descent(plan.handle, arr_o, arr_t, w.C, w.sigma, w.noise_seed, 0,
+                                         DESCENT_LR, DESCENT_L, wsp, sp)
+        else:
+            rc = lib.dpsgd_noise(plan.handle, arr_o, w.C, w.sigma, w.noise_seed, 0, wsp, sp)
+        if rc:
+            dp._check(rc)
+
+    def step(i):
+        for c in calls[i % len(calls)]:
+            c()
+        if w.n_phys > 1:
+            noise_call()
+
+    for i in range(max(args.warmup, len(calls))):
+        step(i)
+    torch.cuda.synchronize()
+    assert dp.status(plan, ws) == dp.OK
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
+
+    gpu_ms, wall_ms = timed(step, args.steps)
+    ms = max(gpu_ms, wall_ms) / args.steps
+    assert dp.status(plan, ws) == dp.OK
+
+    # each phase alone (norms and the GEMM clipped sum cycle through the same batches as the steps)
+    flat_batches = [b for bs in cycle for b in bs]
+    marsh = [(dp._ptr_array(A), dp._ptr_array(G)) for A, G in flat_batches]
+
+    def checked(rc):
+        if rc:
+            dp._check(rc)
+
+    def norms_fn(i):
+        a, g = marsh[i % len(marsh)]
+        checked(lib.dpsgd_norms(plan.handle, w.B, 0, L, a, g, wsp, sp))
+
+    def clip_fn(i):
+        checked(lib.dpsgd_clip(plan.handle, w.B, w.C, 0, wsp, None, None, sp))
+
+    def sum_fn(i):
+        a, g = marsh[i % len(marsh)]
+        checked(lib.dpsgd_clipped_sum(plan.handle, w.B, 0, L, a, g, None, arr_o, 0, wsp, sp))
+
+    reps = args.steps
+    phase_ms = {}
+    phase_ms["norms"] = timed(norms_fn, reps)[0] / reps
+    phase_ms["clip"] = timed(clip_fn, reps)[0] / reps
+    work = algorithmic_work(w, plan, dp)
+    has_gemm = work["clipped_sum"][0] > 0
+    has_stored = work["stored_write"] > 0
+    if has_gemm:
+        norms_fn(0)   # the stored blocks (if any) and factors of batch 0 for the sum phase
+        clip_fn(0)
+        phase_ms["clipped_sum"] = timed(sum_fn, reps)[0] / reps
+    phase_ms["noise"] = timed(lambda i: noise_call(), reps)[0] / reps
+    phase_ms["rest_of_step"] = max(ms - phase_ms["norms"] * w.n_phys, 0.0)
+    torch.cuda.synchronize()
+    assert dp.status(plan, ws) == dp.OK
+
+    # per-phase rooflines; the dominant kernel: the GEMM clipped sum when the plan has one (the
+    # north_star's MFMA GEMM A^T diag(c) G), else the norm kernel
+    kernels = {}
+    for ph in ("norms", "clipped_sum", "noise"):
+        if ph in phase_ms:
+            nb, nf = work[ph]
+            kernels[ph] = phase_roofline(ph, nb, nf, phase_ms[ph], w.dtype)
+    kernels["norms"]["kernel"] = kernel_name("norms", w, plan, dp)
+    kernels["norms"]["launches"] = norm_launches(w, plan, dp)
+    if has_stored:
+        kernels["norms"]["stored_bytes_written"] = work["stored_write"]
+        kernels["norms"]["GBps_incl_stored"] = (work["norms"][0] + work["stored_write"]) / (
+            phase_ms["norms"] * 1e-3) / 1e9
+    if "clipped_sum" in kernels:
+        kernels["clipped_sum"]["kernel"] = kernel_name("clipped_sum", w, plan, dp)
+    dom = "clipped_sum" if has_gemm else "norms"
+    k = kernels[dom]
+    if k["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": k["TFLOPs"], "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": k["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k["hbm_frac"]}
+    launches = k.get("launches", 1)
+    roof["traffic"] = stored_traffic(w.name, dom, SUM_NAMES[sum_policy])
+    roof["kernel"] = k["kernel"]
+    roof["phase"] = dom
+    roof["launches_per_phase"] = launches
+    roof["algorithmic_bytes_per_launch"] = work[dom][0] / launches
+    roof["algorithmic_flops_per_launch"] = work[dom][1] / launches
+    roof["avg_ms"] = phase_ms[dom] / launches
+    if roof["unit"] == "GB/s":
+        try:
+            roof["achievable"] = achievable_hbm(torch, dev, dp)
+            roof["frac_of_achievable"] = roof["achieved"] / roof["achievable"]["read_gbs"]
+            ab = work[dom][0]
+            if N_SETS * ab < torch.cuda.mem_get_info()[0] // 2:
+                roof["achievable_at_size"] = achievable_hbm_at(torch, dev, dp, ab)
+            else:
+                roof["achievable_at_size"] = achievable_hbm_tensors(torch, dp, batches[0])
+            roof["frac_of_achievable_at_size"] = roof["achieved"] / roof["achievable_at_size"]["read_gbs"]
+        except torch.cuda.OutOfMemoryError:
+            pass
+    if has_stored:
+        roof["stored_gradient_blocks"] = {
+            "bytes_written": work["stored_write"], "bytes_read": work["stored_read"],
+            "note": "per-record gradient blocks [d_in x d_out] fp32 that the norm kernel writes "
+                    "and the fused sum + noise kernel reads back instead of re-reading A and G "
+                    "(the STORED clipped-sum strategy); not algorithmic bytes"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del batches, cycle, calls, flat_batches, marsh
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {"metric": METRIC, "value": w.logical_B / (ms * 1e-3), "unit": "records/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": datagen.configs.DTYPE_NAMES[w.dtype],
+            "data": "synthetic",
+            "config": {"workload": w.name, "layers": L, "params": w.n_params,
+                       "records_per_step": w.logical_B, "physical_batches": w.n_phys,
+                       "tokens": w.T, "C": w.C, "sigma": w.sigma,
+                       "sum_policy": args.sum,
+                       "sum_strategy": ("stored" if has_stored and not has_gemm else
+                                        "gemm" if has_gemm and not has_stored else "mixed"),
+                       "parallelism": "single GPU",
+                       "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
+            "roofline": roof, "cpu_baseline": cpu,
+            "phases_ms": phase_ms, "kernels": kernels,
+            "gpu_ms_per_step": gpu_ms / args.steps, "wall_ms_per_step": wall_ms / args.steps,
+            "input_batches": n_cycle}
+    print(json.dumps(line), flush=True)
+    if args.manifest:
+        man = {"git": subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True,
+                                     text=True).stdout.strip() or None,
+               "torch": torch.__version__, "hip": torch.version.hip,
+               "device": torch.cuda.get_device_name(0),
+               "cu": torch.cuda.get_device_properties(0).multi_processor_count,
+               "host_cpu": platform.processor(), "nproc": os.cpu_count(),
+               "plan_paths": [plan.layer_info(l) for l in range(L)], "workload": w.name}
+        with open(args.manifest, "w") as f:
+            json.dump(man, f, indent=1)
+
+
+def kernel_mode(args, w, torch, dev, dp, datagen):
+    """Only the dominant kernel's phase (or --phase), --warmup + --steps times over the workload's
+    first physical batch: the command the HBM byte counters are collected on."""
+    sum_policy = SUM_POLICIES[args.sum]
+    plan = dp.Plan(w.layers, w.dtype, w.B, w.T, dp.PATH_AUTO, sum_policy)
+    ws = plan.workspace(dev)
+    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
+    As, Gs = device_inputs(w, datagen, torch, dev, 0, w.B)
+    work = algorithmic_work(w, plan, dp)
+    phase = args.phase or ("clipped_sum" if work["clipped_sum"][0] > 0 else "norms")
+    L = w.n_layers
+    if phase == "clipped_sum":
+        dp.norms(plan, w.B, 0, L, As, Gs, ws)
+        dp.clip(plan, w.B, w.C, ws)
+    for _ in range(args.warmup + args.steps):
+        if phase == "norms":
+            dp.norms(plan, w.B, 0, L, As, Gs, ws)
+        elif phase == "clipped_sum":
+            dp.clipped_sum(plan, w.B, 0, L, As, Gs, None, out, ws)
+        else:
+            dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws)
+    torch.cuda.synchronize()
+    launches = norm_launches(w, plan, dp) if phase == "norms" else None
+    print(json.dumps({"mode": "kernel", "workload": w.name, "phase": phase, "sum_policy": args.sum,
+                      "calls": args.warmup + args.steps, "launches_per_call": launches,
+                      "algorithmic_bytes_per_call": work[phase][0],
+                      "src_hash": kernel_src_hash(PHASE_SOURCES.get(phase, NORM_KERNEL_SOURCES))}),
+          flush=True)
+
+
+def achievable_hbm_tensors(torch, dp, batch, reps=3):
+    """The streaming read (dpsgd_hbm_read) over the workload's own input tensors, one launch per
+    tensor in turn, best of `reps` passes timed with HIP events: the read rate of the same bytes
+    when the workload is too large to copy for distinct buffers."""
+    As, Gs = batch
+    ts = [t for t in As + Gs if (t.numel() * t.element_size()) % 16 == 0]
+    nb = sum(t.numel() * t.element_size() for t in ts)
+    sink = torch.empty(dp.HBM_READ_SINK_WORDS, dtype=torch.int32, device=ts[0].device)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for t in ts:
+            dp.hbm_read(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr())
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    return {"read_gbs": nb / best / 1e9, "bytes": nb, "us": best * 1e6,
+            "how": f"dpsgd_hbm_read over the workload's {len(ts)} input tensors in turn "
+                   f"({nb / 1e9:.1f} GB), best of {reps} passes"}
 
 
 def sample_line(args, torch, dev, dp):
@@ -248,156 +589,6 @@ def users_line(args, w, torch, dev, dp, datagen):
     print(json.dumps(line), flush=True)
 
 
-def secondary(args, w, torch, dev, dp, datagen):
-    """Secondary lines for workloads 1, 3, 4, 5: one step = all physical batches of a logical
-    batch (virtual batching: norms/clip/sum per physical batch, noise once), inputs resident in
-    HBM; workload 3 streams layer chunks when all inputs do not fit beside the workspace, and then
-    times only the device phases (staging excluded).  Per-phase times come from HIP events."""
-    import numpy as np
-    L = w.n_layers
-    plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
-    ws = plan.workspace(dev)
-    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
-    theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
-             if args.descent else None)
-    e = 4 if w.dtype == 0 else 2
-    in_bytes = w.input_bytes_per_batch()
-    free = torch.cuda.mem_get_info()[0]
-    stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    phase = {"norms": 0.0, "rest_of_step": 0.0}
-    note = ""
-    n_cycle = 1
-    if w.n_phys * in_bytes < free - (8 << 30):
-        batches = [device_inputs(w, datagen, torch, dev, p * w.B, w.B) for p in range(w.n_phys)]
-        # one physical batch: the timed steps cycle through N_SETS distinct batches when they fit,
-        # so that no step re-reads inputs a previous step left in the last-level cache
-        cycle = [batches]
-        if w.n_phys == 1 and N_SETS * in_bytes < (free - (8 << 30)) // 2:
-            cycle += [[device_inputs(w, datagen, torch, dev, k * w.B, w.B)] for k in range(1, N_SETS)]
-        turn = [0]
-        n_cycle = len(cycle)
-
-        def step():
-            bs = cycle[turn[0] % len(cycle)]
-            turn[0] += 1
-            for p, (As, Gs) in enumerate(bs):
-                flags = (dp.NO_NOISE if w.n_phys > 1 else 0) | (dp.ACCUMULATE if p else 0)
-                last = w.n_phys == 1
-                dp.step(plan, As, Gs, out, ws, w.C, w.sigma, w.noise_seed, 0, flags=flags,
-                        params=theta if last else None, lr=DESCENT_LR, normalizer=DESCENT_L)
-            if w.n_phys > 1:
-                dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws, params=theta,
-                         lr=DESCENT_LR, normalizer=DESCENT_L)
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(args.steps):
-            step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / args.steps
-        As, Gs = batches[0]
-
-        def timed(fn):
-            x0, x1 = ev(), ev()
-            x0.record(stream)
-            for _ in range(args.steps):
-                fn()
-            x1.record(stream)
-            torch.cuda.synchronize()
-            return x0.elapsed_time(x1) / args.steps
-        # each phase alone on physical batch 0 (K back-to-back calls between HIP events), with
-        # the C calls' arguments marshalled once so that the host does not pace the GPU
-        lib = dp.load()
-        arr_a, arr_g, arr_o = dp._ptr_array(As), dp._ptr_array(Gs), dp._ptr_array(out)
-        wsp, sp = ws.data_ptr(), stream.cuda_stream
-
-        def checked(rc):
-            if rc:
-                dp._check(rc)
-        phase["norms"] = timed(lambda: checked(lib.dpsgd_norms(plan.handle, w.B, 0, L, arr_a, arr_g,
-                                                               wsp, sp))) * w.n_phys
-        phase["clip"] = timed(lambda: checked(lib.dpsgd_clip(plan.handle, w.B, w.C, 0, wsp, None,
-                                                             None, sp))) * w.n_phys
-        phase["clipped_sum"] = timed(lambda: checked(lib.dpsgd_clipped_sum(
-            plan.handle, w.B, 0, L, arr_a, arr_g, None, arr_o, 0, wsp, sp))) * w.n_phys
-        phase["noise"] = timed(lambda: dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws,
-                                                params=theta, lr=DESCENT_LR, normalizer=DESCENT_L))
-        phase["rest_of_step"] = ms - phase["norms"]   # residual: the step minus the norms timed alone
-    else:
-        # layer-chunk streaming: chunks of inputs filled (untimed), norms timed per chunk
-        note = "layer-chunk streaming, staging excluded"
-        chunk = 32
-        ms_norm = 0.0
-        for l0 in range(0, L, chunk):
-            l1 = min(L, l0 + chunk)
-            As = [None] * (l1 - l0)
-            Gs = [None] * (l1 - l0)
-            for l in range(l0, l1):
-                for tensor, lst in ((0, As), (1, Gs)):
-                    scale, heavy = datagen.record_params(w, l, tensor, 0, w.B)
-                    ds = torch.from_numpy(scale).to(dev)
-                    dh = torch.from_numpy(heavy.astype(np.uint8)).to(dev)
-                    d = w.layers[l][0] if tensor == 0 else w.layers[l][1]
-                    buf = torch.empty((w.B, w.T, d), dtype=torch.int16 if e == 2 else torch.float32, device=dev)
-                    datagen.device_fill(w, l, tensor, buf.data_ptr(), 0, w.B, ds.data_ptr(), dh.data_ptr(),
-                                        stream.cuda_stream)
-                    lst[l - l0] = buf
-            torch.cuda.synchronize()
-            for _ in range(max(1, args.warmup // 4)):
-                dp.norms(plan, w.B, l0, l1, As, Gs, ws)
-            x0, x1 = ev(), ev()
-            x0.record(stream)
-            for _ in range(args.steps):
-                dp.norms(plan, w.B, l0, l1, As, Gs, ws)
-            x1.record(stream)
-            torch.cuda.synchronize()
-            ms_norm += x0.elapsed_time(x1) / args.steps
-            del As, Gs
-        y0, y1 = ev(), ev()
-        y0.record(stream)
-        for _ in range(args.steps):
-            dp.clip(plan, w.B, w.C, ws)
-            dp.clipped_sum(plan, w.B, 0, L, None, None, None, out, ws)
-            dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws, params=theta, lr=DESCENT_LR,
-                     normalizer=DESCENT_L)
-        y1.record(stream)
-        torch.cuda.synchronize()
-        phase["norms"] = ms_norm
-        phase["rest_of_step"] = y0.elapsed_time(y1) / args.steps
-        ms = ms_norm + phase["rest_of_step"]
-    assert dp.status(plan, ws) == dp.OK
-    work = algorithmic_work(w, plan, dp)
-    nb, nf = work["norms"]
-    nb *= w.n_phys
-    nf *= w.n_phys
-    try:
-        ach = achievable_hbm(torch, dev, dp)
-    except torch.cuda.OutOfMemoryError:
-        ach = None
-    norm_gbs = nb / (phase["norms"] * 1e-3) / 1e9
-    line = {"metric": METRIC, "value": w.logical_B / (ms * 1e-3), "unit": "records/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": datagen.configs.DTYPE_NAMES[w.dtype],
-            "data": "synthetic",
-            "config": {"workload": w.name, "layers": L, "params": w.n_params,
-                       "records_per_step": w.logical_B, "physical_batches": w.n_phys, "tokens": w.T,
-                       "parallelism": "single GPU", "note": note,
-                       "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
-            "phases_ms": phase, "input_batches": n_cycle,
-            "norms_roofline": {"hbm_GBps": norm_gbs, "hbm_frac": norm_gbs / HBM_PEAK_GBS,
-                               "frac_of_achievable": norm_gbs / ach["read_gbs"] if ach else None,
-                               "TFLOPs": nf / (phase["norms"] * 1e-3) / 1e12},
-            "hbm_achievable": ach,
-            "clipped_sum_roofline": sum_roofline(work, w, phase),
-            "clipped_sum_bytes": work["clipped_sum"][0] * w.n_phys}
-    print(json.dumps(line), flush=True)
-
-
-N_SETS = 4   # distinct input batches the headline's timed steps cycle through
 I8_PEAK_TOPS = 5000.0   # dense INT8 MFMA, ops/s x 1e-12
 
 
@@ -658,20 +849,23 @@ def achievable_hbm_at(torch, dev, dp, nbytes, n_bufs=N_SETS, reps=40):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="2 (default) is the configuration the metric is quoted on; the others "
-                         "print secondary lines")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5],
+                    help="3 (default): the largest configuration that fits one GPU")
+    ap.add_argument("--sum", default="auto", choices=sorted(SUM_POLICIES),
+                    help="clipped-sum strategy: auto (per-record gradient blocks kept by the norm "
+                         "pass where that moves fewer bytes), gemm (A^T diag(c) G re-reading A and "
+                         "G), stored")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--manifest", default=None, help="write a run manifest JSON here")
     ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy", "sample", "int8"],
-                    help="step: the benchmark; kernel: only the dominant kernel, --steps times "
-                         "(for counter collection); copy: a plain device copy of --copy-mib MiB "
-                         "(the reference for scaling HBM byte counters)")
+                    help="step: the benchmark; kernel: only the dominant kernel's phase (or "
+                         "--phase), --warmup + --steps times (for counter collection); copy: a "
+                         "plain device copy of --copy-mib MiB (the reference for scaling HBM byte "
+                         "counters)")
+    ap.add_argument("--phase", default=None, choices=["norms", "clipped_sum", "noise"])
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--users", action="store_true",
                     help="workload 2's layers with user-level clipping: 16 users of 1-4 records each "
@@ -715,136 +909,11 @@ def main():
     if args.mode == "int8":
         return int8_line(args, torch, dev, dp)
     w = datagen.workload(args.workload)
-    if args.mode == "step" and args.users:
-        return users_line(args, w, torch, dev, dp, datagen)
-    if args.mode == "step" and args.workload != 2:
-        return secondary(args, w, torch, dev, dp, datagen)
-    plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
-    ws = plan.workspace(dev)
-    As, Gs = device_inputs(w, datagen, torch, dev, 0, w.B)
-    out = [torch.empty(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
-    L = w.n_layers
-    stream = torch.cuda.current_stream()
-    # the timed steps cycle through N_SETS distinct batches (records k B .. k B + B - 1 of the
-    # generator), so that no step re-reads inputs a previous step left in the last-level cache
-    sets = [(As, Gs)] + ([device_inputs(w, datagen, torch, dev, k * w.B, w.B) for k in range(1, N_SETS)]
-                         if args.mode == "step" else [])
-
+    if args.users:
+        return users_line(args, datagen.workload(2), torch, dev, dp, datagen)
     if args.mode == "kernel":
-        for _ in range(args.warmup + args.steps):
-            dp.norms(plan, w.B, 0, L, As, Gs, ws)
-        torch.cuda.synchronize()
-        print(json.dumps({"mode": "kernel", "workload": w.name, "launches": args.warmup + args.steps,
-                          "algorithmic_bytes": algorithmic_work(w, plan, dp)["norms"][0]}), flush=True)
-        return
-
-    theta = ([torch.zeros(di * do, dtype=torch.float32, device=dev) for di, do in w.layers]
-             if args.descent else None)
-    calls = [dp.StepCall(plan, A, G, out, ws, w.C, w.sigma, w.noise_seed, 0, params=theta,
-                         lr=DESCENT_LR, normalizer=DESCENT_L) for A, G in sets]
-    for i in range(max(args.warmup, len(calls))):
-        calls[i % len(calls)]()
-    torch.cuda.synchronize()
-    assert dp.status(plan, ws) == dp.OK
-
-    # timed region 1: K whole steps (dpsgd_step: norms -> clip -> clipped sum -> noise), each on
-    # the next batch of the cycle
-    def timed_steps(cs):
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(args.steps):
-            cs[i % len(cs)]()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop), time.perf_counter() - t0
-    gpu_ms, wall = timed_steps(calls)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    assert dp.status(plan, ws) == dp.OK
-    # the same batch every step, for comparison (its inputs partly stay in the last-level cache)
-    gpu1, wall1 = timed_steps(calls[:1])
-    same_ms = max(gpu1, wall1 * 1e3) / args.steps
-
-    # timed region 2: the dominant kernel (the norm launch of the same step, same buffers, the
-    # same cycle of batches), K launches back to back between two HIP events on the stream they
-    # run on: the average holds the kernel and the gap to the next dispatch, not the events'
-    # own recording
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        A, G = sets[i % len(sets)]
-        dp.norms(plan, w.B, 0, L, A, G, ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    phase_ms = {"norms": e0.elapsed_time(e1) / args.steps}
-    phase_ms["rest_of_step"] = max(ms_per_step - phase_ms["norms"], 0.0)
-
-    work = algorithmic_work(w, plan, dp)
-    dom = "norms"
-    nbytes, nflops = work[dom]
-    dur_s = phase_ms[dom] * 1e-3
-    if nflops and nflops / max(nbytes, 1) > MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": nflops / dur_s / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": nbytes / dur_s / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    tpath = args.traffic or os.path.join(ROOT, "profiles", "norm_kernel_traffic.json")
-    if os.path.exists(tpath):
-        # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a plain copy of
-        # known size), valid only while the kernel sources are the ones it was measured on
-        tr = json.load(open(tpath))
-        if (tr.get("kernel_phase") == dom and tr.get("workload") == w.name
-                and tr.get("src_hash") == kernel_src_hash()):
-            roof["traffic"] = tr.get("bytes_per_launch")
-    if roof["unit"] == "GB/s":
-        roof["achievable"] = achievable_hbm(torch, dev, dp)
-        roof["frac_of_achievable"] = roof["achieved"] / roof["achievable"]["read_gbs"]
-        in_bytes = sum(t.numel() * t.element_size() for t in As + Gs)
-        roof["achievable_at_size"] = achievable_hbm_at(torch, dev, dp, in_bytes)
-        roof["frac_of_achievable_at_size"] = roof["achieved"] / roof["achievable_at_size"]["read_gbs"]
-    roof["kernel"] = {"norms": "k_norm_direct (ghost_norm, direct path)",
-                      "clipped_sum": "clipped_sum", "noise": "k_noise"}[dom]
-    roof["algorithmic_bytes"] = nbytes
-    roof["avg_ms"] = phase_ms[dom]
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
-
-    value = w.B / (ms_per_step * 1e-3)
-    line = {
-        "metric": METRIC, "value": value, "unit": "records/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": datagen.configs.DTYPE_NAMES[w.dtype], "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.n_layers, "params": w.n_params,
-                   "records_per_step": w.B, "tokens": w.T, "C": w.C, "sigma": w.sigma,
-                   "parallelism": "single GPU",
-                   "descent": {"lr": DESCENT_LR, "normalizer": DESCENT_L} if args.descent else None},
-        "roofline": roof, "cpu_baseline": cpu,
-        "phases_ms": phase_ms, "gpu_ms_per_step": gpu_ms / args.steps,
-        "wall_ms_per_step": wall * 1e3 / args.steps,
-        "input_batches": len(sets),
-        "same_batch": {"value": w.B / (same_ms * 1e-3), "ms_per_step": same_ms,
-                       "note": "every timed step on one batch; its inputs partly stay in the last-level cache"},
-    }
-    print(json.dumps(line), flush=True)
-    if args.manifest:
-        man = {"git": subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True,
-                                     text=True).stdout.strip() or None,
-               "torch": torch.__version__, "hip": torch.version.hip,
-               "device": torch.cuda.get_device_name(0),
-               "cu": torch.cuda.get_device_properties(0).multi_processor_count,
-               "host_cpu": platform.processor(), "nproc": os.cpu_count(),
-               "plan_paths": [plan.layer_info(l) for l in range(L)], "workload": w.name}
-        with open(args.manifest, "w") as f:
-            json.dump(man, f, indent=1)
+        return kernel_mode(args, w, torch, dev, dp, datagen)
+    return step_line(args, w, torch, dev, dp, datagen)
 
 
 if __name__ == "__main__":

@@ -23,20 +23,48 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_headline_algorithmic_bytes():
-    """Workload 2 (48 fp32 LoRA layers, 16 records x 128 tokens): the norm kernel reads every A
-    and G once (305,135,616 bytes) and writes each record's gradient blocks once (16 x 294,912 x 4
-    bytes)."""
+    """The default workload is 3 (the largest configuration that fits one GPU): 256 bf16 LoRA
+    layers, 256 records x 512 tokens.  The norm kernel's algorithmic bytes are one read of every
+    A and G (275,951,648,768 bytes); the per-record gradient blocks of the STORED strategy
+    (256 x 16,777,216 x 4 bytes written, as many read back) are reported apart."""
+    assert bench.DEFAULT_WORKLOAD == 3
+    w = datagen.workload(3)
+    plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
+    work = bench.algorithmic_work(w, plan, dp)
+    inputs = sum(w.B * w.T * (di + do) * 2 for di, do in w.layers)
+    assert inputs == 275_951_648_768
+    assert work["norms"][0] == inputs
+    assert work["stored_write"] == work["stored_read"] == 256 * 16_777_216 * 4
+    assert work["clipped_sum"] == [0, 0]          # every layer keeps its blocks
+    assert work["noise"][0] == 8 * 16_777_216
+    assert bench.norm_launches(w, plan, dp) == 6  # 256 layers, at most 48 a launch
+    # the GEMM strategy: the sum re-reads every A and G, 2 B T d_in d_out flops per layer
+    g = dp.Plan(w.layers, w.dtype, w.B, w.T, dp.PATH_AUTO, dp.SUM_GEMM)
+    wg = bench.algorithmic_work(w, g, dp)
+    assert wg["stored_write"] == 0 and wg["norms"][0] == inputs
+    assert wg["clipped_sum"] == [inputs + 16_777_216 * 4, 2 * 256 * 512 * 16_777_216]
+
+
+def test_workload2_algorithmic_bytes():
+    """Workload 2 (48 fp32 LoRA layers, 16 records x 128 tokens): 305,135,616 bytes of inputs read
+    once by the norm kernel, in one launch."""
     w = datagen.workload(2)
     plan = dp.Plan(w.layers, w.dtype, w.B, w.T)
     work = bench.algorithmic_work(w, plan, dp)
-    inputs = sum(w.B * w.T * (di + do) * 4 for di, do in w.layers)
-    assert inputs == 305_135_616
-    assert work["norms"][0] == inputs + w.B * 294_912 * 4 == 324_009_984
+    assert work["norms"][0] == 305_135_616
+    assert work["stored_write"] == w.B * 294_912 * 4
     assert all(plan.layer_info(l)[1] == dp.SUM_STORED for l in range(w.n_layers))
+    assert bench.norm_launches(w, plan, dp) == 1
 
 
-@pytest.mark.parametrize("path,names", [("norm_kernel_traffic.json", bench.NORM_KERNEL_SOURCES),
-                                        ("int8_gemm_traffic.json", bench.I8_KERNEL_SOURCES)])
+def _traffic_records():
+    recs = [(f, bench.PHASE_SOURCES[json.load(open(os.path.join(ROOT, "profiles", f)))["kernel_phase"]])
+            for f in sorted(os.listdir(os.path.join(ROOT, "profiles")))
+            if f.startswith("traffic_") and f.endswith(".json")]
+    return recs + [("int8_gemm_traffic.json", bench.I8_KERNEL_SOURCES)]
+
+
+@pytest.mark.parametrize("path,names", _traffic_records())
 def test_traffic_records_follow_the_sources(path, names, tmp_path):
     """A record carries the hash of the sources it was measured on; any edit of them changes the
     hash, so the bench line drops the record instead of reporting stale counters."""

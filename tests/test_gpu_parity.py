@@ -323,6 +323,15 @@ def test_full_workload_exact_oracle(idx):
     ref = _oracle(w, As, Gs)
     r = gpu_step(w, As, Gs, DEV)
     _check_step(w, r, ref, f"full w{idx}")
+    # the pre-noise clipped sum (noise of norm sigma C sqrt(P) would hide its errors: about 543
+    # against at most B C = 16 on workload 2), for the default plan and for the GEMM sum
+    # A^T diag(c) G that re-reads the inputs instead of keeping per-record gradient blocks
+    for sp in (dp.SUM_AUTO, dp.SUM_GEMM):
+        r0 = gpu_step(w, As, Gs, DEV, flags=dp.NO_NOISE, sum_policy=sp)
+        e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
+        say(f"  pre-noise sum (sum policy {sp}): {e0:.2e}")
+        assert r0["status"] == dp.OK and e0 <= TOL[w.dtype]
+        assert max_rel(r0["n"], ref["n"]) <= TOL[w.dtype] and max_rel(r0["c"], ref["c"]) <= TOL[w.dtype]
     if idx == 1:
         # workload 1 spans both clip branches: records 0-3 unclipped, 4-7 clipped
         assert np.all(ref["c"][:4] == 1.0) and np.all(ref["c"][4:] < 1.0)
