@@ -34,7 +34,8 @@ PLAN_SEGMENTS = 1
 
 EXPORTS = ("dpsgd_plan_create", "dpsgd_plan_destroy", "dpsgd_plan_layer_info",
            "dpsgd_plan_num_params", "dpsgd_ws_init", "dpsgd_ws_segments", "dpsgd_norms", "dpsgd_clip",
-           "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_status",
+           "dpsgd_clipped_sum", "dpsgd_noise", "dpsgd_noise_descent", "dpsgd_step", "dpsgd_step_noalloc",
+           "dpsgd_status",
            "dpsgd_layer_norm2",
            "dpsgd_philox_raw", "dpsgd_hbm_read", "dpsgd_poisson_ws_bytes", "dpsgd_poisson_sample",
            "dpsgd_rdp_sampled_gaussian", "dpsgd_rdp_to_epsilon", "dpsgd_gaussian_pair_delta",
@@ -99,6 +100,7 @@ def load():
         "dpsgd_noise": (ctypes.c_int, [P, PP, D, D, U64, U64, P, P]),
         "dpsgd_noise_descent": (ctypes.c_int, [P, PP, PP, D, D, U64, U64, D, D, P, P]),
         "dpsgd_step": (ctypes.c_int, [P, ctypes.POINTER(StepArgs), P]),
+        "dpsgd_step_noalloc": (ctypes.c_int, [P, ctypes.POINTER(StepArgs), P, P]),
         "dpsgd_status": (ctypes.c_int, [P, P, P]),
         "dpsgd_layer_norm2": (ctypes.c_int, [P, I64, I32, I32, P, P, P]),
         "dpsgd_philox_raw": (ctypes.c_int, [U64, U64, U64, U64, P, P]),
@@ -252,6 +254,23 @@ def step(plan: Plan, A, G, out, ws, C: float, sigma: float, seed: int, step_idx:
     args = StepArgs(n, a_arr, g_arr, o_arr, _ptr(ws), C, sigma, seed, step_idx, flags,
                     _ptr(norms_out), _ptr(clip_out), p_arr, lr, normalizer)
     _check(load().dpsgd_step(plan.handle, ctypes.byref(args), _stream(stream)))
+
+
+def step_noalloc(plan: Plan, A, G, out, C: float, sigma: float, seed: int, step_idx: int,
+                 n_records: Optional[int] = None, flags: int = 0, norms_out=None, clip_out=None,
+                 status_out=None, stream=None, params=None, lr: float = 0.0,
+                 normalizer: float = 1.0):
+    """dpsgd_step_noalloc: dpsgd_step on the library's per-device scratch (no workspace
+    argument, no allocation); status_out: optional device uint32 receiving the status word."""
+    n = plan.max_records if n_records is None else n_records
+    a_arr, g_arr, o_arr = _ptr_array(A), _ptr_array(G), _ptr_array(out)
+    p_arr = _ptr_array(params)
+    if params is not None:
+        flags |= DESCENT
+    args = StepArgs(n, a_arr, g_arr, o_arr, None, C, sigma, seed, step_idx, flags,
+                    _ptr(norms_out), _ptr(clip_out), p_arr, lr, normalizer)
+    _check(load().dpsgd_step_noalloc(plan.handle, ctypes.byref(args), _ptr(status_out),
+                                     _stream(stream)))
 
 
 class StepCall:

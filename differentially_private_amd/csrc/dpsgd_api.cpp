@@ -806,9 +806,10 @@ int dpsgd_noise_descent(const dpsgd_plan* p, float* const* out, float* const* pa
     return do_noise(p, out, params, lr / normalizer, C, sigma, seed, step, ws, (hipStream_t)stream);
 }
 
-int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
-    if (int rc = check_plan(p)) return rc;
-    if (!a) return fail(DPSGD_ERR_INVALID_ARG, "args is NULL");
+namespace {
+
+// every host-side check of dpsgd_step's arguments (plan and args non-null)
+int check_step_args(const dpsgd_plan* p, const dpsgd_step_args* a) {
     if (int rc = check_records(p, a->n_records)) return rc;
     if (int rc = check_c_sigma(a->C, a->sigma, true)) return rc;
     if (int rc = check_ws(a->ws)) return rc;
@@ -818,8 +819,6 @@ int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
         return fail(DPSGD_ERR_INVALID_ARG, "DPSGD_DESCENT releases the sum: it needs the noise phase");
     if (descend)
         if (int rc = check_descent(p, a->params, a->lr, a->normalizer)) return rc;
-    float* const* params = descend ? a->params : nullptr;
-    const double descent = descend ? a->lr / a->normalizer : 0.0;
     const int L = (int)p->layers.size();
     if (!a->out) return fail(DPSGD_ERR_INVALID_ARG, "out array is NULL");
     if (a->n_records > 0 && (!a->A || !a->G)) return fail(DPSGD_ERR_INVALID_ARG, "A or G array is NULL");
@@ -827,7 +826,15 @@ int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
         if (!a->out[l]) return fail(DPSGD_ERR_INVALID_ARG, "null out pointer");
         if (a->n_records > 0 && (!a->A[l] || !a->G[l])) return fail(DPSGD_ERR_INVALID_ARG, "null A or G pointer");
     }
-    hipStream_t s = (hipStream_t)stream;
+    return DPSGD_OK;
+}
+
+// the step's launches (arguments already checked)
+int run_step(const dpsgd_plan* p, const dpsgd_step_args* a, hipStream_t s) {
+    const bool descend = (a->flags & DPSGD_DESCENT) != 0;
+    float* const* params = descend ? a->params : nullptr;
+    const double descent = descend ? a->lr / a->normalizer : 0.0;
+    const int L = (int)p->layers.size();
     if (int rc = do_norms(p, a->n_records, 0, L, a->A, a->G, a->ws, s)) return rc;
     if (a->n_records > 0 && all_stored(p))
         return do_finalize(p, a->n_records, a->C, a->sigma, a->seed, a->step, a->flags, a->ws,
@@ -836,6 +843,45 @@ int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
     if (int rc = do_sum(p, a->n_records, 0, L, a->A, a->G, nullptr, a->out, a->flags, a->ws, s)) return rc;
     if (!(a->flags & DPSGD_NO_NOISE))
         if (int rc = do_noise(p, a->out, params, descent, a->C, a->sigma, a->seed, a->step, a->ws, s)) return rc;
+    return DPSGD_OK;
+}
+
+}  // namespace
+
+int dpsgd_step(const dpsgd_plan* p, const dpsgd_step_args* a, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (!a) return fail(DPSGD_ERR_INVALID_ARG, "args is NULL");
+    if (int rc = check_step_args(p, a)) return rc;
+    return run_step(p, a, (hipStream_t)stream);
+}
+
+int dpsgd_step_noalloc(const dpsgd_plan* p, const dpsgd_step_args* a, uint32_t* status_out, void* stream) {
+    if (int rc = check_plan(p)) return rc;
+    if (!a) return fail(DPSGD_ERR_INVALID_ARG, "args is NULL");
+    if (a->ws) return fail(DPSGD_ERR_INVALID_ARG, "dpsgd_step_noalloc uses the library's scratch: args->ws must be NULL");
+    if (p->segments)
+        return fail(DPSGD_ERR_INVALID_ARG, "segment plans need their offsets in a caller workspace (dpsgd_ws_segments)");
+    if (p->ws_bytes > kScratchBytes)
+        return fail(DPSGD_ERR_INVALID_ARG, "the plan's workspace (" + std::to_string(p->ws_bytes) +
+                                               " bytes) exceeds the library's scratch of " +
+                                               std::to_string(kScratchBytes) + " bytes");
+    if (status_out && reinterpret_cast<uintptr_t>(status_out) % 4)
+        return fail(DPSGD_ERR_INVALID_ARG, "status_out must be 4-byte aligned");
+    // the same host checks as dpsgd_step, on a copy of the arguments that names a placeholder
+    // workspace, so that every argument error is returned before the scratch is looked up
+    dpsgd_step_args b = *a;
+    b.ws = reinterpret_cast<void*>(kAlign);
+    if (int rc = check_step_args(p, &b)) return rc;
+    void* scratch = nullptr;
+    hipError_t e = scratch_pointer(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+    b.ws = scratch;
+    hipStream_t s = (hipStream_t)stream;
+    if (int rc = run_step(p, &b, s)) return rc;
+    if (status_out) {
+        e = launch_status_copy(ws_status(scratch, p), status_out, s);
+        if (e != hipSuccess) return hip_fail(e, "status copy launch");
+    }
     return DPSGD_OK;
 }
 

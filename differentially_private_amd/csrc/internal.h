@@ -188,6 +188,9 @@ static_assert(sizeof(DirectArgs) <= 4096 && sizeof(GramArgs) <= 4096 && sizeof(R
                   sizeof(LayerNormArgs) <= 4096,
               "kernel arguments travel by value and must stay under 4 KB");
 
+// Size of the fixed device scratch that dpsgd_step_noalloc uses in place of a caller workspace.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s);
 hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s);
@@ -201,6 +204,9 @@ hipError_t launch_layer_norm2(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, bool clip_inside, hipStream_t s);
 hipError_t launch_sum_dense(const DenseSumArgs& a, int n_splits, hipStream_t s);
+// device address of this device's scratch (looked up once per device)
+hipError_t scratch_pointer(void** out);
+hipError_t launch_status_copy(const uint32_t* status, uint32_t* out, hipStream_t s);
 
 // privacy accounting (host)
 double rdp_sampled_gaussian(double q, double sigma, double alpha);

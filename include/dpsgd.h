@@ -218,6 +218,25 @@ int dpsgd_noise_descent(const dpsgd_plan* plan, float* const* out, float* const*
  * the first, then dpsgd_noise (or dpsgd_noise_descent) once. */
 int dpsgd_step(const dpsgd_plan* plan, const dpsgd_step_args* args, void* stream);
 
+/* dpsgd_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches as dpsgd_step, with the workspace taken from a scratch area of
+ * 64 MiB (67,108,864 bytes) that the library holds on each device it runs on
+ * from the code object's load until the process ends.  args->ws must be NULL.
+ * Returns DPSGD_ERR_INVALID_ARG, before any launch, for a plan whose ws_bytes
+ * exceed 64 MiB or that was created with DPSGD_PLAN_SEGMENTS, and for every
+ * argument error dpsgd_step reports.  status_out (optional device uint32,
+ * 4-byte aligned) receives the step's status word after the step (0, or nonzero
+ * when a norm was NaN/Inf and the sum and noise were skipped), written by a
+ * one-thread kernel on `stream`.  Calls no allocating routine.  Every call on a
+ * device shares that device's scratch and leaves its contents (partials,
+ * factors, gradient blocks, status) for the next call: calls that overlap on one
+ * device (other streams or threads) race.  With DPSGD_ACCUMULATE the status is
+ * OR-ed with the previous call's, as in a virtual batch on one workspace; a call
+ * without it resets the status. */
+int dpsgd_step_noalloc(const dpsgd_plan* plan, const dpsgd_step_args* args, uint32_t* status_out,
+                       void* stream);
+
 /* Poisson sampling of a step's records ("Privacy-Preserving Machine Learning",
  * DP-SGD phase 1: each of `population` records included independently with
  * public probability q, 0 <= q <= 1).  Record i draws word i mod 4 of
