@@ -458,29 +458,49 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
     return DPSGD_OK;
 }
 
-// params (or null): the descent step params_l -= descent * out_l after the noise
+// params (or null): the descent step params_l -= descent * out_l after the noise.  The layers are
+// cut into pieces of at most kNoisePieceMax elements and go out in as few launches as the
+// kernel-argument limit allows (one for every plan of this library's workloads), each launch's
+// pieces spanning less than 2^32 elements.
 int do_noise(const dpsgd_plan* p, float* const* out, float* const* params, double descent, double C,
              double sigma, uint64_t seed, uint64_t step, const void* ws, hipStream_t s) {
-    const int L = (int)p->layers.size();
-    const int per = balanced_chunk(L, kNoiseMaxLayers);
+    struct Piece { float* out; float* par; int64_t off, n; };
+    std::vector<Piece> pieces;
+    for (size_t l = 0; l < p->layers.size(); ++l) {
+        const LayerPlan& lp = p->layers[l];
+        for (int64_t x = 0; x < lp.n_params; x += kNoisePieceMax) {
+            const int64_t n = std::min<int64_t>(kNoisePieceMax, lp.n_params - x);
+            pieces.push_back({out[l] + x, params ? params[l] + x : nullptr, lp.param_off + x, n});
+        }
+    }
+    const int cap = params ? kNoiseMaxPiecesDescent : kNoiseMaxPieces;
+    const int per = balanced_chunk((int)pieces.size(), cap);
     NoiseArgs a;
-    for (int l0 = 0; l0 < L; l0 += per) {
-        const int l1 = std::min(L, l0 + per);
+    size_t k = 0;
+    while (k < pieces.size()) {
         std::memset(&a, 0, sizeof(a));
-        a.n_layers = l1 - l0;
+        a.base = pieces[k].off;
         a.seed = seed;
         a.step = step;
         a.scale = (float)(sigma * C);
         a.descent = (float)descent;
         a.status = ws ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + p->status_off) : nullptr;
-        for (int l = l0; l < l1; ++l) {
-            a.out[l - l0] = out[l];
-            a.params[l - l0] = params ? params[l] : nullptr;
-            a.off[l - l0] = p->layers[l].param_off;
+        a.with_params = params ? 1 : 0;
+        int n = 0;
+        while (k + n < pieces.size() && n < per &&
+               pieces[k + n].off + pieces[k + n].n - a.base <= (int64_t)UINT32_MAX) {
+            a.off[n] = (uint32_t)(pieces[k + n].off - a.base);
+            ++n;
         }
-        a.off[l1 - l0] = p->layers[l1 - 1].param_off + p->layers[l1 - 1].n_params;
+        a.n_pieces = n;
+        a.off[n] = (uint32_t)(pieces[k + n - 1].off + pieces[k + n - 1].n - a.base);
+        for (int q = 0; q < n; ++q) {
+            a.ptr[q] = pieces[k + q].out;
+            if (params) a.ptr[n + q] = pieces[k + q].par;
+        }
         hipError_t e = launch_noise(a, s);
         if (e != hipSuccess) return hip_fail(e, "noise launch");
+        k += n;
     }
     return DPSGD_OK;
 }

@@ -9,7 +9,6 @@
 namespace dpsgd {
 
 constexpr int kMaxLaunchLayers = 48;  // per-launch layer descriptors (kernarg <= 4 KB)
-constexpr int kNoiseMaxLayers = 128;  // NoiseArgs stays under 4 KB (checked below)
 
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
@@ -99,16 +98,22 @@ struct ReduceArgs {
     int64_t max_n4;      // max over layers of ceil(n / 4)
 };
 
+// One noise launch covers up to kNoiseMaxPieces pieces of layers (a layer of more than
+// kNoisePieceMax elements is cut into pieces of that size), each with its out pointer and, for the
+// descent step, its parameter pointer, so that a whole LoRA plan goes out in one launch.
+constexpr int kNoiseMaxPieces = 320;                     // without the descent step
+constexpr int kNoiseMaxPiecesDescent = 160;              // with it (two pointers per piece)
+constexpr int64_t kNoisePieceMax = (int64_t)1 << 30;     // elements per piece (a multiple of 4)
 struct NoiseArgs {
-    float* out[kNoiseMaxLayers];
-    int64_t off[kNoiseMaxLayers + 1];  // flat offsets of the launch's layers, off[0] = first flat index
-    int32_t n_layers;
-    int32_t pad;
+    int64_t base;                      // flat index of the launch's first element
     uint64_t seed, step;
+    const uint32_t* status;
     float scale;                       // sigma * C
     float descent;                     // lr / normalizer (with params)
-    const uint32_t* status;
-    float* params[kNoiseMaxLayers];    // descent step targets, or all null
+    int32_t n_pieces;
+    int32_t with_params;               // ptr[n_pieces + k]: parameters of piece k
+    uint32_t off[kNoiseMaxPieces + 1]; // flat offsets relative to base, off[0] = 0
+    float* ptr[kNoiseMaxPieces];       // out pointers of the pieces, then (with_params) theirs
 };
 static_assert(sizeof(NoiseArgs) <= 4096, "kernel arguments of the noise launch exceed 4 KB");
 

@@ -11,24 +11,28 @@
 // r sin(2 pi u2), r = sqrt(-2 ln u1).  Both uniforms are exact in fp32.  One
 // thread per four consecutive elements of a layer (one Philox block when the
 // layer starts on a multiple of 4); the add is a coalesced read-modify-write.
+// One launch covers every layer of a plan up to the kernel-argument limit (320 layers, 160 with
+// the descent step), so a LoRA plan's noise is one pass over the flat index.
 #include <algorithm>
 
 #include "philox.h"
 
 namespace dpsgd {
 
-// Grid: x = 256-thread chunks of a layer (4 elements per thread), y = layer.
+// Grid: x = 256-thread chunks of a piece (4 elements per thread), y = piece.
 __global__ __launch_bounds__(256) void k_noise(NoiseArgs a) {
     if (a.status && *a.status) return;
     const int l = blockIdx.y;
-    const int64_t off = a.off[l];
-    const int64_t n_l = a.off[l + 1] - off;
+    const int64_t off = a.base + a.off[l];
+    const int64_t n_l = (int64_t)(a.off[l + 1] - a.off[l]);
     const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (x0 >= n_l) return;
-    float* o = a.out[l] + x0;
-    float* th = a.params[l] ? a.params[l] + x0 : nullptr;   // descent step target
+    float* const out_l = a.ptr[l];
+    float* const par_l = a.with_params ? a.ptr[a.n_pieces + l] : nullptr;
+    float* o = out_l + x0;
+    float* th = par_l ? par_l + x0 : nullptr;   // descent step target
     if (x0 + 4 <= n_l && (off & 3) == 0 && (n_l & 3) == 0 &&
-        ((reinterpret_cast<uintptr_t>(a.out[l]) | reinterpret_cast<uintptr_t>(a.params[l])) & 15u) == 0) {
+        ((reinterpret_cast<uintptr_t>(out_l) | reinterpret_cast<uintptr_t>(par_l)) & 15u) == 0) {
         float z[4];
         gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
         f32x4 v = *reinterpret_cast<f32x4*>(o);
@@ -65,9 +69,9 @@ __global__ __launch_bounds__(256) void k_philox_raw(uint64_t seed, uint64_t step
 
 hipError_t launch_noise(const NoiseArgs& a, hipStream_t s) {
     int64_t max_n = 0;
-    for (int l = 0; l < a.n_layers; ++l) max_n = std::max<int64_t>(max_n, a.off[l + 1] - a.off[l]);
+    for (int l = 0; l < a.n_pieces; ++l) max_n = std::max<int64_t>(max_n, (int64_t)(a.off[l + 1] - a.off[l]));
     if (max_n == 0) return hipSuccess;
-    const dim3 grid((unsigned)((max_n + 1023) / 1024), a.n_layers);
+    const dim3 grid((unsigned)((max_n + 1023) / 1024), a.n_pieces);
     hipLaunchKernelGGL(k_noise, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -31,8 +31,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint64_t block, uint64_t step, 
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
         const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
         const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-        const uint32_t y0 = hi1 ^ x1 ^ k0;
-        const uint32_t y2 = hi0 ^ x3 ^ k1;
+        // three-input XORs as one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+        const uint32_t y0 = __builtin_amdgcn_bitop3_b32(hi1, x1, k0, 0x96);
+        const uint32_t y2 = __builtin_amdgcn_bitop3_b32(hi0, x3, k1, 0x96);
         x0 = y0;
         x1 = lo1;
         x2 = y2;
@@ -43,14 +44,17 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint64_t block, uint64_t step, 
     return o;
 }
 
+// r = sqrt(-2 ln u1) with -2 ln u1 = (-2 ln 2) log2 u1, and the angle 2 pi u2, from the hardware's
+// log2 and its sine and cosine, which take their argument in revolutions (sin(2 pi x) for x): u1
+// in [2^-24, 1] is never denormal and u2 in [0, 1) needs no range reduction.  Checked on every one
+// of the 2^24 uniforms against float64: log2 within 1.2e-7 relative (next to u1 = 1 as well), sine
+// and cosine within 2.1 * 2^-24 absolute, so |Z - Z_exact| stays within 5.3 * 2^-24 (1 + |Z|).
 __device__ __forceinline__ void box_muller(uint32_t we, uint32_t wo, float& z_even, float& z_odd) {
     const float u1 = (float)((we >> 8) + 1u) * 0x1.0p-24f;
     const float u2 = (float)(wo >> 8) * 0x1.0p-24f;
-    const float r = sqrtf(-2.0f * logf(u1));
-    float sn, cs;
-    sincospif(2.0f * u2, &sn, &cs);
-    z_even = r * cs;
-    z_odd = r * sn;
+    const float r = sqrtf(-1.38629436111989061883f * __builtin_amdgcn_logf(u1));
+    z_even = r * __builtin_amdgcn_cosf(u2);
+    z_odd = r * __builtin_amdgcn_sinf(u2);
 }
 
 

@@ -83,6 +83,34 @@ def test_noise_pure_z_and_statistics():
     assert abs(np.linalg.norm(z_gpu) - math.sqrt(d)) < 5 / math.sqrt(2)
 
 
+@pytest.mark.parametrize("descent", [False, True])
+def test_noise_many_layers_several_launches(descent):
+    """700 layers of 1-60 x 1-9 elements (ragged flat offsets): more layers than one noise launch
+    takes (320, or 160 with the descent step), so the stream crosses launch boundaries; every
+    coordinate against the oracle's, and the descent step on every parameter."""
+    rng = np.random.default_rng(700 + descent)
+    layers = [(int(rng.integers(1, 61)), int(rng.integers(1, 10))) for _ in range(700)]
+    say("noise many layers", len(layers), "descent", descent)
+    base = [rng.standard_normal(a * b).astype(np.float32) for a, b in layers]
+    plan, out = _noise_plan_and_out(layers, base)
+    sigma, C, seed, step, lr, L = 0.9, 1.7, 77, 5, 0.25, 4.0
+    theta0 = [rng.standard_normal(a * b).astype(np.float32) for a, b in layers]
+    theta = [torch.from_numpy(t).to(DEV) for t in theta0] if descent else None
+    dp.noise(plan, out, C, sigma, seed, step, params=theta, lr=lr, normalizer=L)
+    got = flat([o.cpu().numpy() for o in out])
+    z = oracle.gauss(seed, step, 0, plan.n_params)
+    z_gpu = (got - flat(base)) / (sigma * C)
+    assert np.all(np.abs(z_gpu - z) <= 8 * 2.0 ** -24 * (1 + np.abs(z)) + 4e-7 * np.abs(flat(base)) / (sigma * C))
+    if descent:
+        # the oracle's update of its own noised sum; the GPU's within 1e-5 of the update's norm
+        # plus the fp32 spacing of the parameters
+        noised = flat(base) + sigma * C * z
+        want = oracle.descent(flat(theta0), noised, lr, L)
+        th = flat([t.cpu().numpy() for t in theta])
+        spacing = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+        assert np.linalg.norm(th - want) <= 1e-5 * np.linalg.norm(want - flat(theta0)) + np.linalg.norm(spacing)
+
+
 def test_noise_sigma_zero_and_step_change():
     layers = [(16, 16)]
     plan, out = _noise_plan_and_out(layers, [np.arange(256, dtype=np.float32)])
