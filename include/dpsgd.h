@@ -126,7 +126,12 @@ typedef struct dpsgd_step_args {
 } dpsgd_step_args;
 
 /* Build a plan: validate shapes, choose the path of every layer and lay out
- * the workspace.  Host only (no device call).  *ws_bytes receives the size of
+ * the workspace.  Host only (no device call).  The plan describes the records
+ * and layers of the clipped sum F(D) = sum_r clip(g_r) of "Sensitivity Inflation
+ * from Cross-Record Precision Routing in Private Quantized Fine-Tuning", Sec. 2
+ * Eqs. 2-3: every record's gradient g_r over all the plan's layers, one norm
+ * per record ("Differential Privacy: DP-SGD, Privacy Budgets, and LLMs", the
+ * combined norm of the concatenated per-example gradient).  *ws_bytes receives the size of
  * the device workspace every call with this plan needs.  Returns
  * DPSGD_ERR_INVALID_ARG for a null pointer, n_layers < 1, a dimension < 1,
  * max_records < 1, T < 1, or sizes whose products overflow 64 bits;
@@ -353,7 +358,10 @@ int dpsgd_i8_intermediates(const dpsgd_i8_plan* plan, const void* ws, int64_t n_
                            int32_t* owner, void* stream);
 
 /* Synchronise `stream` and read the status word: DPSGD_OK or
- * DPSGD_ERR_NONFINITE (or DPSGD_ERR_HIP). */
+ * DPSGD_ERR_NONFINITE (or DPSGD_ERR_HIP).  A record whose norm is not finite
+ * cannot be clipped to the bound ("Privacy-Preserving Machine Learning": its
+ * clip_vector_l2 example refuses non-finite coordinates and a norm that
+ * overflows); the kernels skip the sum and the noise and report it here. */
 int dpsgd_status(const dpsgd_plan* plan, const void* ws, void* stream);
 
 /* Per-layer squared norms of layers [l0, l1) from the partials of the last
@@ -364,7 +372,12 @@ int dpsgd_layer_norm2(const dpsgd_plan* plan, int64_t n_records, int32_t l0, int
                       const void* ws, float* out, void* stream);
 
 /* Raw Philox4x32-10 words of blocks first_block .. first_block + n_blocks - 1
- * for key = seed and counter = (block, step): 4 * n_blocks uint32 at dev_out. */
+ * for key = seed and counter = (block, step): 4 * n_blocks uint32 at dev_out.
+ * The words behind the noise N(0, sigma^2 C^2 I) of DP-SGD phase 4
+ * ("Privacy-Preserving Machine Learning"); the pages fix no generator (the
+ * sensitivity paper's release audit, Sec. 6.5, uses the framework's own), so the
+ * stream is Philox4x32-10 (Salmon et al., SC'11), exported for bit-exact
+ * comparison with an independent implementation. */
 int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_t n_blocks,
                      uint32_t* dev_out, void* stream);
 
