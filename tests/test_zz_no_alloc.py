@@ -134,3 +134,40 @@ def test_noalloc_refuses_large_and_segment_plans():
     assert lib.dpsgd_step_noalloc(big.handle, ctypes.byref(args), None, None) == dp.ERR_INVALID_ARG
     seg = dp.Plan([(8, 8)], dp.DTYPE_F32, 2, 4, segments=True)
     assert lib.dpsgd_step_noalloc(seg.handle, ctypes.byref(args), None, None) == dp.ERR_INVALID_ARG
+
+
+def test_noalloc_step_in_a_hip_graph():
+    """The use the entry point is for: the whole step (norms, clip factors, the fused sum + noise or
+    the GEMM sum, the status copy) captured once into a HIP graph, which no allocation may enter,
+    then replayed on new inputs copied into the same buffers, with eager steps and
+    synchronisations between the replays; every replay equals the eager dpsgd_step on a caller
+    workspace bit for bit."""
+    for w, sp in ((datagen.reduced(2), dp.SUM_AUTO), (datagen.reduced(3), dp.SUM_GEMM)):
+        say("noalloc graph", w.name, sp)
+        plan = dp.Plan(w.layers, w.dtype, w.B, w.T, dp.PATH_AUTO, sp)
+        As, Gs = host_inputs(w)
+        dA = [to_device(a, DEV) for a in As]
+        dG = [to_device(g, DEV) for g in Gs]
+        out = [torch.zeros(a * b, dtype=torch.float32, device=DEV) for a, b in w.layers]
+        nrm = torch.zeros(w.B, dtype=torch.float32, device=DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            dp.step_noalloc(plan, dA, dG, out, w.C, w.sigma, 9, 4, norms_out=nrm, status_out=st,
+                            stream=cap)
+        for k in range(3):
+            A2, G2 = host_inputs(w, first=w.B * (k + 1), n=w.B)
+            for d, h in zip(dA + dG, A2 + G2):
+                d.copy_(to_device(h, DEV))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = ([o.cpu().numpy().copy() for o in out], nrm.cpu().numpy().copy(), int(st.cpu().numpy()[0]))
+            ref = _run(plan, w, dA, dG, w.B, noalloc=False, seed=9, step=4)
+            assert got[2] == 0 and ref["status"] == 0
+            assert np.array_equal(got[1], ref["n"])
+            for x, y in zip(got[0], ref["out"]):
+                assert np.array_equal(x, y)
+        del g
