@@ -111,6 +111,34 @@ def test_noise_many_layers_several_launches(descent):
         assert np.linalg.norm(th - want) <= 1e-5 * np.linalg.norm(want - flat(theta0)) + np.linalg.norm(spacing)
 
 
+def test_noise_flat_index_past_2_32():
+    """A 65,536 x 65,536 layer (2^32 parameters, cut into four launch pieces of 2^30) followed by a
+    5 x 7 layer whose flat offsets start at 2^32: the Philox counter's upper word and the launch
+    split by span.  Every coordinate of the small layer, and runs of coordinates at the start, the
+    piece boundaries and the end of the large one, against the oracle's stream."""
+    free = torch.cuda.mem_get_info()[0]
+    if free < (20 << 30):
+        pytest.skip("needs 20 GB of free device memory")
+    layers = [(65536, 65536), (5, 7)]
+    say("noise past 2^32")
+    plan = dp.Plan(layers, dp.DTYPE_F32, 1, 1)
+    big = torch.zeros(1 << 32, dtype=torch.float32, device=DEV)
+    small = torch.zeros(35, dtype=torch.float32, device=DEV)
+    sigma, C, seed, step = 1.5, 0.5, 0xABCDEF0123456789, 2**40 + 3
+    dp.noise(plan, [big, small], C, sigma, seed, step)
+    torch.cuda.synchronize()
+    sc = sigma * C
+    z = oracle.gauss(seed, step, 1 << 32, 35)
+    got = small.cpu().numpy().astype(np.float64) / sc
+    assert np.all(np.abs(got - z) <= 8 * 2.0 ** -24 * (1 + np.abs(z)))
+    for start in (0, (1 << 30) - 37, (1 << 31) - 5, 3 * (1 << 30) - 64, (1 << 32) - 41):
+        n = 101 if start + 101 <= (1 << 32) else (1 << 32) - start
+        got = big[start:start + n].cpu().numpy().astype(np.float64) / sc
+        want = oracle.gauss(seed, step, start, n)
+        assert np.all(np.abs(got - want) <= 8 * 2.0 ** -24 * (1 + np.abs(want))), start
+    del big
+
+
 def test_noise_sigma_zero_and_step_change():
     layers = [(16, 16)]
     plan, out = _noise_plan_and_out(layers, [np.arange(256, dtype=np.float32)])
