@@ -59,6 +59,19 @@ __device__ __forceinline__ int code_of(float a, float s) {
     return s == 0.f ? 0 : (int)rintf(div_rn(127.f * a, s));
 }
 
+// Fast form of code_of for a row of scale s, given r127 = fl(127 fl(1 / s)) with the hardware
+// reciprocal (good to 1 ulp; r127 = 0 when s = 0): q0 = fl(a r127) is within 2^-22 |q| of the
+// exact quotient q = 127 a / s, so for |q0| < 128 within 2^-15 + 2^-17 of the correctly rounded
+// quotient d.  Where q0 is more than 2^-13 away from every half-integer, rint(q0) = rint(d) =
+// code_of(a, s); code_fast reports the other elements (rare; always for NaN or infinity), which
+// take code_of itself.
+__device__ __forceinline__ float code_fast(float a, float r127, bool& exact) {
+    const float q0 = a * r127;
+    const float k = rintf(q0);
+    exact = fabsf(q0) < 128.f && fabsf(q0 - k) < 0.5f - 0x1p-13f;
+    return k;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -68,7 +81,7 @@ __device__ __forceinline__ float wave_max(float v) {
 }  // namespace
 
 // Row blocks: record r owns max(1, ceil(len / 16)) blocks of up to 16 of its rows, numbered from
-// boff[r]; a workgroup takes one block, four rows per wavefront.
+// boff[r]; a workgroup takes one block, one row per wavefront.
 constexpr int kScanRows = 16;
 
 struct RowBlock {
@@ -93,15 +106,19 @@ __device__ __forceinline__ bool row_block(const I8Args& a, RowBlock& rb) {
     return true;
 }
 
-// Rows of a block per wavefront, and 16-byte chunks per row and lane loaded together: all of a
-// wavefront's loads for up to RPW rows x CPL chunks are issued before any is used.
-constexpr int RPW = kScanRows / 4;
-constexpr int CPL = 2;
+// The routing kernels run one row of a block per wavefront (sixteen wavefronts per workgroup, so
+// that four are resident per SIMD), and a lane loads CPL 16-byte chunks of its row together: all
+// of a wavefront's loads for up to RPW rows x CPL chunks (a whole row of up to 3072 columns) are
+// issued before any is used.
+constexpr int kRouteWaves = 16;
+constexpr int kRouteThreads = 64 * kRouteWaves;
+constexpr int RPW = kScanRows / kRouteWaves;
+constexpr int CPL = 6;
 
 // Per block: each row's owner and scale s_i = max |a| over the entries below tau, and the block's
 // partial outlier mask (the OR of its rows' per-entry tests |a| >= tau, taken in LDS) written
 // whole with plain stores, so nothing needs clearing between calls.
-__global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
+__global__ __launch_bounds__(kRouteThreads) void k_i8_scan(I8Args a) {
     __shared__ uint32_t wm[kI8MaxKW];
     RowBlock rb;
     if (!row_block(a, rb)) return;
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
         for (int j = 0; j < RPW; ++j)
 #pragma unroll
             for (int b = 0; b < CPL; ++b) {
-                const int rr = w + 4 * j;
+                const int rr = w + kRouteWaves * j;
                 const int64_t c = c0 + 64 * b;
                 const bool ok = rr < rb.nrows && c < nch;
                 const uint16_t* x = a.A + (rb.row0 + (ok ? rr : 0)) * a.K + 8 * (ok ? c : 0);
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
             }
     };
     if (vec) load(lane);
-    for (int t = tid; t < KW; t += 256) wm[t] = 0u;
+    for (int t = tid; t < KW; t += kRouteThreads) wm[t] = 0u;
     __syncthreads();
     if (vec) {
         for (int64_t c0 = lane; c0 < nch; c0 += 64 * CPL) {
@@ -153,7 +170,7 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
         }
     } else {
         for (int j = 0; j < RPW; ++j) {
-            const int rr = w + 4 * j;
+            const int rr = w + kRouteWaves * j;
             if (rr >= rb.nrows) break;
             const uint16_t* x = a.A + (rb.row0 + rr) * a.K;
             for (int64_t k = lane; k < a.K; k += 64) {
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
     }
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-        const int rr = w + 4 * j;
+        const int rr = w + kRouteWaves * j;
         const float m = wave_max(mx[j]);
         if (lane == 0 && rr < rb.nrows) {
             a.s[rb.row0 + rr] = m;
@@ -174,24 +191,25 @@ __global__ __launch_bounds__(256) void k_i8_scan(I8Args a) {
     }
     __syncthreads();
     uint32_t* pm = a.pmask + (int64_t)blockIdx.x * KW;
-    for (int t = tid; t < KW; t += 256) pm[t] = wm[t];
+    for (int t = tid; t < KW; t += kRouteThreads) pm[t] = wm[t];
 }
 
 // Per block: the record's outlier set O_r = OR of its blocks' partial masks (in LDS; the record's
 // first block also writes it out for the GEMM), then the codes of the block's rows in Q (pitch
 // Kp bytes, zero past K): round(127 a / s_i), zero in O_r's columns.
-__global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
+__global__ __launch_bounds__(kRouteThreads) void k_i8_quant(I8Args a) {
     __shared__ uint32_t om[kI8MaxKW];
     RowBlock rb;
     if (!row_block(a, rb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int KW = (int)a.KW;
     const int64_t* boff = a.offsets + a.n_rec + 1;
-    float sj[RPW];
+    float sj[RPW], rj[RPW];
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-        const int rr = w + 4 * j;
+        const int rr = w + kRouteWaves * j;
         sj[j] = rr < rb.nrows ? a.s[rb.row0 + rr] : 0.f;
+        rj[j] = sj[j] == 0.f ? 0.f : 127.f * __builtin_amdgcn_rcpf(sj[j]);
     }
     const bool vec = rb.nrows > 0 && a.a_vec;
     const int64_t nch = a.K / 8, npc = a.Kp / 8;
@@ -203,7 +221,7 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
         for (int j = 0; j < RPW; ++j)
 #pragma unroll
             for (int b = 0; b < CPL; ++b) {
-                const int rr = w + 4 * j;
+                const int rr = w + kRouteWaves * j;
                 const int64_t c = c0 + 64 * b;
                 const bool ok = rr < rb.nrows && c < nch;
                 const uint16_t* x = a.A + (rb.row0 + (ok ? rr : 0)) * a.K + 8 * (ok ? c : 0);
@@ -211,18 +229,21 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
             }
     };
     if (vec) load(lane);
-    for (int t = tid; t < KW; t += 256) om[t] = 0u;
+    for (int t = tid; t < KW; t += kRouteThreads) om[t] = 0u;
     __syncthreads();
-    const int64_t b0 = boff[rb.r];
-    const int64_t pairs = (boff[rb.r + 1] - b0) * KW;
+    // thread t ORs word t % KW of blocks t / KW, t / KW + NT / KW, ... of the record
+    const int64_t b0 = boff[rb.r], nb = boff[rb.r + 1] - b0;
     const uint32_t* pr = a.pmask + b0 * KW;
-    for (int64_t q = tid; q < pairs; q += 256) {
-        const uint32_t m = pr[q];
-        if (m) atomicOr(om + (int)(q % KW), m);
+    {
+        const int wd = tid % KW, bs = kRouteThreads / KW;
+        uint32_t m = 0;
+        if (tid < bs * KW)
+            for (int64_t b = tid / KW; b < nb; b += bs) m |= pr[b * KW + wd];
+        if (m) atomicOr(om + wd, m);
     }
     __syncthreads();
     if ((int64_t)blockIdx.x == b0)
-        for (int t = tid; t < KW; t += 256) a.omask[rb.r * KW + t] = om[t];
+        for (int t = tid; t < KW; t += kRouteThreads) a.omask[rb.r * KW + t] = om[t];
     if (vec) {
         for (int64_t c0 = lane; c0 < npc; c0 += 64 * CPL) {
             if (c0 != lane) load(c0);
@@ -230,16 +251,32 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
             for (int j = 0; j < RPW; ++j)
 #pragma unroll
                 for (int b = 0; b < CPL; ++b) {
-                    const int rr = w + 4 * j;
+                    const int rr = w + kRouteWaves * j;
                     const int64_t c = c0 + 64 * b;
                     if (rr >= rb.nrows || c >= npc) continue;
                     uint32_t lo = 0, hi = 0;
                     if (c < nch) {
                         const uint32_t m = om[(8 * c) / 32] >> ((8 * c) % 32);
+                        float k[8];
+                        bool all_exact = true;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float f = h2f(v[j][b][e >> 1] >> (16 * (e & 1)));
-                            const int code = ((m >> e) & 1u) ? 0 : code_of(f, sj[j]);
+                            bool ex;
+                            k[e] = code_fast(h2f(v[j][b][e >> 1] >> (16 * (e & 1))), rj[j], ex);
+                            all_exact = all_exact && ex;
+                        }
+                        if (!all_exact) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float f = h2f(v[j][b][e >> 1] >> (16 * (e & 1)));
+                                bool ex;
+                                code_fast(f, rj[j], ex);
+                                if (!ex) k[e] = (float)code_of(f, sj[j]);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int code = ((m >> e) & 1u) ? 0 : (int)k[e];
                             const uint32_t bb = (uint32_t)(code & 0xFF) << (8 * (e & 3));
                             if (e < 4) lo |= bb;
                             else hi |= bb;
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(256) void k_i8_quant(I8Args a) {
         }
     } else {
         for (int j = 0; j < RPW; ++j) {
-            const int rr = w + 4 * j;
+            const int rr = w + kRouteWaves * j;
             if (rr >= rb.nrows) break;
             const int64_t row = rb.row0 + rr;
             const uint16_t* x = a.A + row * a.K;
@@ -597,8 +634,8 @@ int64_t i8_scan_blocks(int64_t n, int64_t n_rec) { return (n + kScanRows - 1) / 
 hipError_t launch_i8_route(const I8Args& a, hipStream_t s) {
     if (a.n_rec > 0) {
         const dim3 g((unsigned)i8_scan_blocks(a.n, a.n_rec));
-        hipLaunchKernelGGL(k_i8_scan, g, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(k_i8_quant, g, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_i8_scan, g, dim3(kRouteThreads), 0, s, a);
+        hipLaunchKernelGGL(k_i8_quant, g, dim3(kRouteThreads), 0, s, a);
     }
     return hipGetLastError();
 }
