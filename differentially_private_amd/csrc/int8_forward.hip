@@ -53,6 +53,14 @@ __device__ __forceinline__ uint16_t f2h_rounded(float x) {
     return f2h(x);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The same rounding as f2h_rounded, as an fp16 value.
+__device__ __forceinline__ _Float16 f16_rounded(float x) {
+    asm volatile("" : "+v"(x));
+    return (_Float16)x;
+}
+
 __device__ __forceinline__ float div_rn(float x, float y) { return __fdiv_rn(x, y); }
 
 __device__ __forceinline__ int code_of(float a, float s) {
@@ -588,16 +596,23 @@ __global__ __launch_bounds__(64 * WI * WO, 1) void k_i8_gemm(I8Args a) {
 #pragma unroll
         for (int f = 0; f < FO; ++f) {
             const int64_t ob = o0 + 16 * FO * wo + 16 * f + 4 * g;
-            uint16_t y[4];
+            // the two fp16 halves are added in fp16, two outputs per instruction: rounding the fp32
+            // sum of two fp16 values to fp16 gives the correctly rounded fp16 sum (fp32 carries
+            // 24 >= 2 x 11 + 2 significand bits), so this is fp16(float(dq16) + float(corr16))
+            uint32_t yw[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float d = h2f(f2h_rounded(((float)acc[f][e][r] * sa) * sbv[f][r]));
-                const float c = h2f(f2h_rounded(corr[f][r]));
-                y[r] = f2h(d + c);
+            for (int r = 0; r < 4; r += 2) {
+                f16x2 dq, co;
+                dq[0] = f16_rounded(((float)acc[f][e][r] * sa) * sbv[f][r]);
+                dq[1] = f16_rounded(((float)acc[f][e][r + 1] * sa) * sbv[f][r + 1]);
+                co[0] = f16_rounded(corr[f][r]);
+                co[1] = f16_rounded(corr[f][r + 1]);
+                yw[r / 2] = __builtin_bit_cast(uint32_t, dq + co);
             }
+            const uint16_t y[4] = {(uint16_t)yw[0], (uint16_t)(yw[0] >> 16), (uint16_t)yw[1],
+                                   (uint16_t)(yw[1] >> 16)};
             uint16_t* dst = a.Y + i * N + ob;
-            const uint2 packed = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16),
-                                            (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+            const uint2 packed = make_uint2(yw[0], yw[1]);
             if (interior) {
                 *reinterpret_cast<uint2*>(dst) = packed;
             } else if (i < n) {
