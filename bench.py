@@ -647,9 +647,9 @@ def int8_model(torch, dev, dp, seed=0):
 def int8_line(args, torch, dev, dp):
     """Record-owned LLM.int8 forward of the OPT-125M backbone (72 INT8 layers, one physical batch
     of 16 x 256 tokens per step): eager and HIP-graph timings of the whole forward, the GEMM's
-    roofline from HIP events around each dpsgd_i8_matmul, the batched LLM.int8 variant (one
-    record spanning the batch: the same kernels with the batch-wide union) for comparison, and
-    the oracle's rate on one layer of each shape."""
+    roofline from HIP events around back-to-back dpsgd_i8_matmul calls of each layer, the batched
+    LLM.int8 variant (one record spanning the batch: the same kernels with the batch-wide union)
+    for comparison, and the oracle's rate on one layer of each shape."""
     import ctypes
     import numpy as np
     m = int8_model(torch, dev, dp)
@@ -712,32 +712,37 @@ def int8_line(args, torch, dev, dp):
     graph_ms = timed(g.replay, args.steps)
     batched_graph_ms = timed(gb.replay, args.steps)
 
-    # dominant kernel: the INT8 GEMM of every layer, HIP events around dpsgd_i8_matmul (the
-    # routing kernels of that layer run untimed just before it)
+    # dominant kernel: the INT8 GEMM of every layer, timed like every other phase: back-to-back
+    # dpsgd_i8_matmul calls of one layer between two HIP events on the stream they run on (the
+    # routing kernels of that layer run untimed before them).  Inside the forward the same GEMMs
+    # run longer: by then the other layers' weights have evicted theirs from the L2.
     ops = 0
     gemm_ms = 0.0
-    reps = max(1, args.steps // 10)
+    per = max(3, args.steps // 5)
     launches = 0
     abytes = 0   # codes + weight codes read, fp16 outputs written (outlier corrections aside)
-    for _ in range(reps):
-        for L in m["layers"]:
-            dp.i8_route(plan, ws, n, B, L["A"], L["K"], 6.0, stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dp.i8_matmul(plan, ws, n, B, L["A"], L["K"], L["wq"], L["sw"], L["N"], L["Y"], stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            gemm_ms += e0.elapsed_time(e1)
-            ops += 2 * n * L["K"] * L["N"]
-            abytes += (n + L["N"]) * dp.i8_pitch(L["K"]) + 2 * n * L["N"]
-            launches += 1
+    for L in m["layers"]:
+        dp.i8_route(plan, ws, n, B, L["A"], L["K"], 6.0, stream)
+        mm = (plan, ws, n, B, L["A"], L["K"], L["wq"], L["sw"], L["N"], L["Y"], stream)
+        dp.i8_matmul(*mm)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per):
+            dp.i8_matmul(*mm)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_ms += e0.elapsed_time(e1)
+        ops += per * 2 * n * L["K"] * L["N"]
+        abytes += per * ((n + L["N"]) * dp.i8_pitch(L["K"]) + 2 * n * L["N"])
+        launches += per
     avg_ms = gemm_ms / launches
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOP/s",
             "frac": achieved / I8_PEAK_TOPS, "traffic": stored_i8_traffic(),
             "kernel": "k_i8_gemm (INT8 MFMA, dequantisation + record-owned FP16 correction)",
             "algorithmic_ops_per_launch": ops / launches, "algorithmic_bytes_per_launch": abytes / launches,
-            "avg_ms": avg_ms, "launches": launches}
+            "avg_ms": avg_ms, "launches": launches,
+            "timing": "back-to-back launches of each layer's GEMM between two HIP events"}
 
     # the same kernels on one 7B-shaped frozen projection (4096 -> 4096) over 16 records x 512
     # tokens, where the INT8 product is large enough for the GEMM's MFMA efficiency to show
