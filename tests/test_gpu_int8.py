@@ -129,6 +129,11 @@ CASES = [
     ("ragged_small_tiles", [130, 97, 51], 200, 261, {"p_owned": 1.0}),
     ("big_tiles", [256] * 16, 72, 4096, {}),
     ("big_tiles_ragged_scalar", [300] * 13 + [137], 100, 4116, {"p_owned": 0.6}),
+    # rows wider than one batch of the routing kernels' loads (3072 columns), ragged: a second,
+    # partial batch; not a multiple of 8: the element-wise path; the largest K the plan takes
+    ("wide_k_two_load_batches", [40, 25, 63], 5000, 96, {"p_owned": 1.0}),
+    ("wide_k_scalar", [17, 30], 6147, 40, {}),
+    ("max_k", [3, 5, 2], 32768, 24, {"p_owned": 1.0}),
 ]
 
 
