@@ -358,7 +358,7 @@ def step_line(args, w, torch, dev, dp, datagen):
     assert dp.status(plan, ws) == dp.OK
 
     # per-phase rooflines; the dominant kernel: the GEMM clipped sum when the plan has one (the
-    # the benchmark spec's MFMA GEMM A^T diag(c) G), else the norm kernel
+    # MFMA GEMM A^T diag(c) G), else the norm kernel
     kernels = {}
     for ph in ("norms", "clipped_sum", "noise"):
         if ph in phase_ms:
