@@ -79,12 +79,12 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
         for (; k + 8 <= a.n_src; k += 8) {     // 8 independent loads in flight, ascending order
             f32x4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(L.src + (k + u) * L.n + e);
+            for (int u = 0; u < 8; ++u) v[u] = load_stream(reinterpret_cast<const f32x4*>(L.src + (k + u) * L.n + e));
 #pragma unroll
             for (int u = 0; u < 8; ++u) add_scaled(d, WEIGHTED ? a.clip[k + u] : 1.f, v[u]);
         }
         for (; k < a.n_src; ++k)
-            add_scaled(d, WEIGHTED ? a.clip[k] : 1.f, *reinterpret_cast<const f32x4*>(L.src + k * L.n + e));
+            add_scaled(d, WEIGHTED ? a.clip[k] : 1.f, load_stream(reinterpret_cast<const f32x4*>(L.src + k * L.n + e)));
         f32x4 s = {(float)d[0], (float)d[1], (float)d[2], (float)d[3]};
         if (a.accumulate) s = *reinterpret_cast<const f32x4*>(L.out + e) + s;
         *reinterpret_cast<f32x4*>(L.out + e) = s;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
     if (VEC || vec) {
 #pragma unroll
         for (int u = 0; u < kFinalBatch; ++u)   // unconditional: rows past n_rec repeat the last
-            v[u] = *reinterpret_cast<const f32x4*>(src + (u < nb0 ? u : nb0 - 1) * n_l);
+            v[u] = load_stream(reinterpret_cast<const f32x4*>(src + (u < nb0 ? u : nb0 - 1) * n_l));
     }
 
     // 3) this thread's normals (Philox + Box-Muller), computed while the loads are in flight
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int64_t r = i + u < a.n_rec ? i + u : a.n_rec - 1;
-                w8[u] = *reinterpret_cast<const f32x4*>(src + r * n_l);
+                w8[u] = load_stream(reinterpret_cast<const f32x4*>(src + r * n_l));
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)

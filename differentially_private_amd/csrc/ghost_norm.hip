@@ -21,8 +21,9 @@ namespace dpsgd {
 
 // fp32, MB = 1 (LoRA shapes): ask for at least 4 wavefronts per SIMD (the kernel
 // then fits 5 without spilling), so that a whole LoRA workload's tiles are
-// resident at once and no tail of late wavefronts is left.
-template <int DT, int MB, bool STORE>
+// resident at once and no tail of late wavefronts is left.  STORE: 0 = norms only,
+// 1 = the gradient blocks written too, 2 = written with non-temporal stores.
+template <int DT, int MB, int STORE>
 __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_direct(DirectArgs args) {
     const DirectLayer& L = args.L[blockIdx.z];
     const int w = threadIdx.x >> 6;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_d
         args.parts[rec * args.parts_stride + L.part_off + tile_y * L.tiles_x + tile_x] = s;
     if (STORE) {
         float* dst = L.P + rec * (int64_t)L.dX * L.dY;
-        direct_store<DT, MB>(dst, L, n0, m0, g, c, acc, false);
+        direct_store<DT, MB, STORE == 2>(dst, L, n0, m0, g, c, acc, false);
     }
 }
 
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
     }
 }
 
-hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store, hipStream_t s) {
+hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, int store, hipStream_t s) {
     int gx = 1;
     for (int l = 0; l < a.n_layers; ++l) {
         const int v = a.L[l].wg_x * a.L[l].tiles_y;
@@ -539,13 +540,20 @@ hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, bool store
     }
     const dim3 grid(gx, (unsigned)a.n_rec, a.n_layers);
 #define DPSGD_LAUNCH(DT, MB, ST) hipLaunchKernelGGL((k_norm_direct<DT, MB, ST>), grid, dim3(64 * a.wpb), 0, s, a)
+#define DPSGD_LAUNCH_ST(DT, MB)                          \
+    do {                                                 \
+        if (store == 2) DPSGD_LAUNCH(DT, MB, 2);         \
+        else if (store == 1) DPSGD_LAUNCH(DT, MB, 1);    \
+        else DPSGD_LAUNCH(DT, MB, 0);                    \
+    } while (0)
     if (dtype == kBF16) {
-        if (mb == 1) { if (store) DPSGD_LAUNCH(kBF16, 1, true); else DPSGD_LAUNCH(kBF16, 1, false); }
-        else { if (store) DPSGD_LAUNCH(kBF16, 2, true); else DPSGD_LAUNCH(kBF16, 2, false); }
+        if (mb == 1) DPSGD_LAUNCH_ST(kBF16, 1);
+        else DPSGD_LAUNCH_ST(kBF16, 2);
     } else {
-        if (mb == 1) { if (store) DPSGD_LAUNCH(kF32, 1, true); else DPSGD_LAUNCH(kF32, 1, false); }
-        else { if (store) DPSGD_LAUNCH(kF32, 2, true); else DPSGD_LAUNCH(kF32, 2, false); }
+        if (mb == 1) DPSGD_LAUNCH_ST(kF32, 1);
+        else DPSGD_LAUNCH_ST(kF32, 2);
     }
+#undef DPSGD_LAUNCH_ST
 #undef DPSGD_LAUNCH
     return hipGetLastError();
 }

@@ -36,7 +36,7 @@ __device__ __forceinline__ void direct_block_bf16(const uint16_t* __restrict__ X
         for (int q = 0; q < 8; ++q) {
             const int64_t t = t0 + 8 * g + q;
             if (t < T && full) {
-                raw[q] = *reinterpret_cast<const u32x4*>(X + t * dX + col);
+                raw[q] = load_stream(reinterpret_cast<const u32x4*>(X + t * dX + col));
             } else {
                 uint32_t w[4] = {0u, 0u, 0u, 0u};
                 if (t < T) {
@@ -94,7 +94,7 @@ __device__ __forceinline__ void load_half_f32(const float* __restrict__ X, const
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (t < T && full[h]) {
-                xv[s][h] = *reinterpret_cast<const f32x4*>(X + t * dX + cols[h]);
+                xv[s][h] = load_stream(reinterpret_cast<const f32x4*>(X + t * dX + cols[h]));
             } else {
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (t < T) {
@@ -176,7 +176,7 @@ __device__ __forceinline__ void direct_block(const void* X, const void* Y, int64
 
 // Write (or add) the block into a [d_in, d_out] row-major fp32 matrix `dst`.
 // Element (m, n) of the block is row m0 + m of Y's columns and column n of X's.
-template <int DT, int MB>
+template <int DT, int MB, bool STREAM = false>
 __device__ __forceinline__ void direct_store(float* __restrict__ dst, const DirectLayer& L, int n0,
                                              int m0, int g, int c, const f32x4 (&acc)[MB][8],
                                              bool add) {
@@ -194,7 +194,8 @@ __device__ __forceinline__ void direct_store(float* __restrict__ dst, const Dire
                 if (mr + 4 <= L.dY && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
                     f32x4 v = acc[mb][idx];
                     if (add) v += *reinterpret_cast<f32x4*>(p);
-                    *reinterpret_cast<f32x4*>(p) = v;
+                    if constexpr (STREAM) store_stream(v, reinterpret_cast<f32x4*>(p));
+                    else *reinterpret_cast<f32x4*>(p) = v;
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -219,7 +220,8 @@ __device__ __forceinline__ void direct_store(float* __restrict__ dst, const Dire
                     if (n + 4 <= L.dX && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
                         f32x4 v = v0;
                         if (add) v += *reinterpret_cast<f32x4*>(p);
-                        *reinterpret_cast<f32x4*>(p) = v;
+                        if constexpr (STREAM) store_stream(v, reinterpret_cast<f32x4*>(p));
+                        else *reinterpret_cast<f32x4*>(p) = v;
                     } else {
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
