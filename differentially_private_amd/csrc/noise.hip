@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_noise(NoiseArgs a) {
         ((reinterpret_cast<uintptr_t>(out_l) | reinterpret_cast<uintptr_t>(par_l)) & 15u) == 0) {
         float z[4];
         gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
-        f32x4 v = load_stream(reinterpret_cast<const f32x4*>(o));
+        f32x4 v = *reinterpret_cast<f32x4*>(o);
         v[0] += a.scale * z[0];
         v[1] += a.scale * z[1];
         v[2] += a.scale * z[2];

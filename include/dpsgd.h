@@ -383,8 +383,8 @@ int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_
 
 /* Measurement aid (not a step of the method): a plain streaming read of `bytes`
  * bytes at device pointer `buf` (16-byte aligned, bytes a positive multiple of
- * 16), the reference for the HBM bandwidth that ordinary 16-byte loads reach on
- * this device.  Writes DPSGD_HBM_READ_SINK_WORDS words to device pointer `sink`
+ * 16), the reference for the HBM bandwidth that 16-byte loads with the
+ * non-temporal hint (as the library's single-use reads are) reach on this device.  Writes DPSGD_HBM_READ_SINK_WORDS words to device pointer `sink`
  * (caller-owned): the XOR of all of them equals the XOR of every 32-bit word of
  * the buffer.  Asynchronous on `stream`; argument errors are returned before any
  * launch. */
