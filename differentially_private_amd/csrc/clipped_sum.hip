@@ -64,8 +64,9 @@ __global__ __launch_bounds__(128) void k_sum_direct(DirectArgs args) {
     direct_store<DT, MB>(dst, L, n0, m0, g, c, sum, add);
 }
 
-// out[e] (+)= sum_k w_k src[k][e], k ascending, accumulated in fp64 and rounded to fp32 once;
-// w_k = clip[k] (STORED) or 1 (split partials).
+// out[e] (+)= sum_k w_k src[k][e'], k ascending, accumulated in fp64 and rounded to fp32 once;
+// w_k = clip[k] (STORED) or 1 (split partials); e' is the position where the blocks keep element
+// e (a thread takes stored positions e' and writes e = stored_logical(e')).
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     if (a.status && *a.status) return;
@@ -86,15 +87,17 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
         for (; k < a.n_src; ++k)
             add_scaled(d, WEIGHTED ? a.clip[k] : 1.f, load_stream(reinterpret_cast<const f32x4*>(L.src + k * L.n + e)));
         f32x4 s = {(float)d[0], (float)d[1], (float)d[2], (float)d[3]};
-        if (a.accumulate) s = *reinterpret_cast<const f32x4*>(L.out + e) + s;
-        *reinterpret_cast<f32x4*>(L.out + e) = s;
+        f32x4* o = reinterpret_cast<f32x4*>(L.out + stored_logical(L.map, e));
+        if (a.accumulate) s = *o + s;
+        *o = s;
     } else {
         for (int64_t x = e; x < e + 4 && x < L.n; ++x) {
             double d = 0.0;
             for (int64_t k = 0; k < a.n_src; ++k)
                 d = fma(WEIGHTED ? (double)a.clip[k] : 1.0, (double)L.src[k * L.n + x], d);
             const float s = (float)d;
-            L.out[x] = a.accumulate ? L.out[x] + s : s;
+            float* o = L.out + stored_logical(L.map, x);
+            *o = a.accumulate ? *o + s : s;
         }
     }
 }

@@ -70,9 +70,25 @@ struct LayerPlan {
     int nb, n_pairs;
     int64_t n_parts, part_off;
     int64_t stored_off;  // bytes into ws (STORED)
+    StoredMap smap;      // order of the STORED blocks, written by the norm kernel
     int64_t split_off;   // bytes into ws (GEMM with splits)
     bool dense;          // GEMM sum on the dense MFMA kernels (bf16, both dimensions > 16)
 };
+
+namespace {
+
+// Order of a layer's STORED gradient blocks (StoredMap): the norm kernel keeps whole 128-wide X
+// tiles in store order when stored_permuted(d_out), the natural order otherwise.
+StoredMap stored_map(int dtype, const LayerPlan& lp) {
+    StoredMap m{0, 0, lp.d_out};
+    if (lp.sum_mode != DPSGD_SUM_STORED || !stored_permuted(lp.d_out)) return m;
+    if (lp.tiles.x_is_in) m.mode = dtype == DPSGD_DTYPE_BF16 ? 1 : 2;
+    else if (dtype == DPSGD_DTYPE_BF16) m.mode = 3;
+    m.full = (int32_t)(lp.tiles.dX / 128 * 128);
+    return m;
+}
+
+}  // namespace
 
 struct dpsgd_plan {
     std::vector<LayerPlan> layers;
@@ -316,6 +332,7 @@ int do_sum(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const
             d.src = (lp.sum_mode == DPSGD_SUM_STORED) ? ws_f(ws, lp.stored_off) : nullptr;
             d.out = out[l - l0];
             d.n = lp.n_params;
+            d.map = lp.smap;
             r.max_n4 = std::max<int64_t>(r.max_n4, (lp.n_params + 3) / 4);
             if (++r.n_layers == kMaxLaunchLayers) {
                 int rc = flush();
@@ -553,6 +570,7 @@ int do_finalize(const dpsgd_plan* p, int64_t n_rec, double C, double sigma, uint
             a.params[l - l0] = params ? params[l] : nullptr;
             a.src[l - l0] = ws_f(ws, p->layers[l].stored_off);
             a.off[l - l0] = p->layers[l].param_off;
+            a.map[l - l0] = p->layers[l].smap;
         }
         a.off[l1 - l0] = p->layers[l1 - 1].param_off + p->layers[l1 - 1].n_params;
         hipError_t e = launch_finalize(a, inside, s);
@@ -700,6 +718,7 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     p->seg_off = region(p->segments ? p->B + 1 : 0, 8);
     p->stored_bytes = 0;
     for (LayerPlan& lp : p->layers) {
+        lp.smap = stored_map(p->dtype, lp);
         if (lp.sum_mode == DPSGD_SUM_STORED) {
             lp.stored_off = region(p->B, lp.n_params * 4);
             if (fits) p->stored_bytes += p->B * lp.n_params * 4;   // bounded by the checked offsets

@@ -25,7 +25,8 @@ constexpr int kFinalMaxThreads = 512;
 
 // Grid: x = chunks of a layer (4 elements per thread, 64 * nw threads, nw chosen by
 // the host so that the grid is about one workgroup per compute unit), y = layer of
-// the launch.  Element x of layer l has flat index off_l + x.  VEC: every layer of the
+// the launch.  A thread reads the blocks at stored positions x .. x + 3 of layer l, which
+// hold its elements xl .. xl + 3 (xl = stored_logical(x)), flat indices off_l + xl.  VEC: every layer of the
 // launch has n_l and off_l multiples of 4 and 16-byte aligned blocks (checked on the
 // host), so the gradient loads are unconditional 16-byte loads (a thread past the end
 // of its layer loads the layer's last four elements and stores nothing).  Loads
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
     const int64_t n_l = a.off[l + 1] - off;
     const int64_t x0 = ((int64_t)blockIdx.x * blockDim.x + tid) * 4;
     const bool active = x0 < n_l;
+    const int64_t xl = active ? stored_logical(a.map[l], x0) : x0;   // the elements' own index
     float* th = a.params[l];   // descent step target, or null
     const bool vec = VEC ? active
                          : active && x0 + 4 <= n_l && (n_l & 3) == 0 && (off & 3) == 0 &&
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
 
     // 3) this thread's normals (Philox + Box-Muller), computed while the loads are in flight
     float z[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.noise && vec) gauss4((uint64_t)(off + x0) >> 2, a.step, a.seed, z);
+    if (a.noise && vec) gauss4((uint64_t)(off + xl) >> 2, a.step, a.seed, z);
 
     // 4) clip factors
     const float* cf = a.clip;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
                 add_scaled(d, keep_or_zero(cf[i + u < a.n_rec ? i + u : 0], i + u < a.n_rec), w8[u]);
         }
         f32x4 s = {(float)d[0], (float)d[1], (float)d[2], (float)d[3]};
-        f32x4* o = reinterpret_cast<f32x4*>(a.out[l] + x0);
+        f32x4* o = reinterpret_cast<f32x4*>(a.out[l] + xl);
         if (a.accumulate) s = *o + s;
         s[0] += a.scale * z[0];
         s[1] += a.scale * z[1];
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
         s[3] += a.scale * z[3];
         *o = s;
         if (th) {
-            f32x4* tp = reinterpret_cast<f32x4*>(th + x0);
+            f32x4* tp = reinterpret_cast<f32x4*>(th + xl);
             f32x4 t = *tp;
 #pragma unroll
             for (int q = 0; q < 4; ++q) t[q] = fmaf(-a.descent, s[q], t[q]);
@@ -142,8 +144,9 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
         return;
     }
     for (int q = 0; q < 4; ++q) {
-        const int64_t x = x0 + q;
-        if (x >= n_l) break;
+        const int64_t xs = x0 + q;             // stored position
+        if (xs >= n_l) break;
+        const int64_t x = stored_logical(a.map[l], xs);
         const uint64_t e = (uint64_t)(off + x);
         float z = 0.f;
         if (a.noise) {
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kFinalMaxThreads) void k_finalize(FinalizeArgs a) {
             z = z4[e & 3];
         }
         double d = 0.0;
-        for (int64_t i = 0; i < a.n_rec; ++i) d = fma((double)cf[i], (double)a.src[l][i * n_l + x], d);
+        for (int64_t i = 0; i < a.n_rec; ++i) d = fma((double)cf[i], (double)a.src[l][i * n_l + xs], d);
         float s = (float)d;
         float* o = a.out[l] + x;
         if (a.accumulate) s = *o + s;

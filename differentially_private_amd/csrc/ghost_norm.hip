@@ -58,7 +58,7 @@ __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_d
         args.parts[rec * args.parts_stride + L.part_off + tile_y * L.tiles_x + tile_x] = s;
     if (STORE) {
         float* dst = L.P + rec * (int64_t)L.dX * L.dY;
-        direct_store<DT, MB, STORE == 2>(dst, L, n0, m0, g, c, acc, false);
+        direct_store<DT, MB, STORE == 2, true>(dst, L, n0, m0, g, c, acc, false);
     }
 }
 

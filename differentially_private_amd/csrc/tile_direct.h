@@ -176,11 +176,14 @@ __device__ __forceinline__ void direct_block(const void* X, const void* Y, int64
 
 // Write (or add) the block into a [d_in, d_out] row-major fp32 matrix `dst`.
 // Element (m, n) of the block is row m0 + m of Y's columns and column n of X's.
-template <int DT, int MB, bool STREAM = false>
+// STORED (per-record gradient blocks in the workspace): the X indices of a whole tile are kept in
+// store order when stored_permuted(d_out) (see StoredMap).
+template <int DT, int MB, bool STREAM = false, bool STORED = false>
 __device__ __forceinline__ void direct_store(float* __restrict__ dst, const DirectLayer& L, int n0,
                                              int m0, int g, int c, const f32x4 (&acc)[MB][8],
                                              bool add) {
     const int64_t d_out = L.d_out;
+    const bool perm = STORED && stored_permuted(d_out) && n0 + 128 <= L.dX;
     if (L.x_is_in) {
         // dst[x_col * d_out + y_row]: the 4 rows r of a lane are consecutive y_row
 #pragma unroll
@@ -190,7 +193,7 @@ __device__ __forceinline__ void direct_store(float* __restrict__ dst, const Dire
             for (int idx = 0; idx < 8; ++idx) {
                 const int n = direct_col<DT>(n0, c, idx);
                 if (n >= L.dX) continue;
-                float* p = dst + (int64_t)n * d_out + mr;
+                float* p = dst + (int64_t)(perm ? n0 + 16 * idx + c : n) * d_out + mr;
                 if (mr + 4 <= L.dY && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
                     f32x4 v = acc[mb][idx];
                     if (add) v += *reinterpret_cast<f32x4*>(p);
@@ -214,7 +217,7 @@ __device__ __forceinline__ void direct_store(float* __restrict__ dst, const Dire
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const int n = direct_col<DT>(n0, c, 4 * q);
-                    float* p = dst + (int64_t)m * d_out + n;
+                    float* p = dst + (int64_t)m * d_out + (perm ? n0 + 64 * q + 4 * c : n);
                     const f32x4 v0 = {acc[mb][4 * q][r], acc[mb][4 * q + 1][r],
                                       acc[mb][4 * q + 2][r], acc[mb][4 * q + 3][r]};
                     if (n + 4 <= L.dX && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
