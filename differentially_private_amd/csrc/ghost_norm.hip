@@ -26,7 +26,7 @@ namespace dpsgd {
 template <int DT, int MB, int STORE>
 __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_direct(DirectArgs args) {
     const DirectLayer& L = args.L[blockIdx.z];
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: the tile origin is uniform
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const int tile_y = blockIdx.x / L.wg_x;
