@@ -37,6 +37,7 @@ MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0}   # dense fp32 / bf16 MFMA
 DEFAULT_WORKLOAD = 3
 N_SETS = 4   # distinct input batches a single-batch workload's timed steps cycle through
 MAX_LAUNCH_LAYERS = 48   # layers per launch of the norm and tile-engine sum kernels (library)
+MAX_DENSE_LAYERS = 32    # per launch of the dense clipped sum (its kernel-argument limit)
 SUM_POLICIES = {"auto": 0, "gemm": 1, "stored": 2}
 SUM_NAMES = {0: "auto", 1: "gemm", 2: "stored"}
 
@@ -82,6 +83,21 @@ def norm_launches(w, plan, dp):
     return sum(-(-n // MAX_LAUNCH_LAYERS) for n in groups.values())
 
 
+def sum_launches(w, plan, dp):
+    """Launches of the GEMM clipped-sum kernels per physical batch: bf16 layers with both
+    dimensions above 16 on the dense MFMA kernel, at most 32 layers a launch; the other GEMM layers
+    on the tile engine in groups of equal MFMA row blocks, at most 48 layers a launch (each followed
+    by its split reduce when the records are split)."""
+    groups = {}
+    for l, (di, do) in enumerate(w.layers):
+        if plan.layer_info(l)[1] != dp.SUM_GEMM:
+            continue
+        key = "dense" if (w.dtype == dp.DTYPE_BF16 and min(di, do) > 16) else ("tile", min(di, do) <= 16)
+        groups[key] = groups.get(key, 0) + 1
+    return sum(-(-n // (MAX_DENSE_LAYERS if k == "dense" else MAX_LAUNCH_LAYERS))
+               for k, n in groups.items())
+
+
 def device_inputs(w, datagen, torch, dev, first, n):
     """Fill A and G of every layer for records [first, first+n) directly in HBM."""
     import numpy as np
@@ -100,12 +116,12 @@ def device_inputs(w, datagen, torch, dev, first, n):
     return As, Gs
 
 
-# sources the ghost-norm kernels are compiled from: a stored HBM-traffic record applies only while
-# these are unchanged
-NORM_KERNEL_SOURCES = ("ghost_norm.hip", "tile_direct.h", "device_common.h", "internal.h")
-# the same for the clipped-sum kernels (tile engine, dense MFMA kernels, split reduce)
+# sources the ghost-norm kernels and their launch configuration (layer grouping, store mode) come
+# from: a stored HBM-traffic record applies only while these are unchanged
+NORM_KERNEL_SOURCES = ("ghost_norm.hip", "tile_direct.h", "device_common.h", "internal.h", "dpsgd_api.cpp")
+# the same for the clipped-sum kernels (tile engine, dense MFMA kernels, split reduce, split counts)
 SUM_KERNEL_SOURCES = ("clipped_sum.hip", "clipped_sum_dense.hip", "tile_direct.h", "device_common.h",
-                      "internal.h")
+                      "internal.h", "dpsgd_api.cpp")
 # the same for the INT8 forward's kernels
 I8_KERNEL_SOURCES = ("int8_forward.hip", "int8.h", "device_common.h", "internal.h")
 PHASE_SOURCES = {"norms": NORM_KERNEL_SOURCES, "clipped_sum": SUM_KERNEL_SOURCES}
@@ -372,6 +388,7 @@ def step_line(args, w, torch, dev, dp, datagen):
             phase_ms["norms"] * 1e-3) / 1e9
     if "clipped_sum" in kernels:
         kernels["clipped_sum"]["kernel"] = kernel_name("clipped_sum", w, plan, dp)
+        kernels["clipped_sum"]["launches"] = sum_launches(w, plan, dp)
     dom = "clipped_sum" if has_gemm else "norms"
     k = kernels[dom]
     if k["bound"] == "mfma":
@@ -485,7 +502,8 @@ def kernel_mode(args, w, torch, dev, dp, datagen):
         else:
             dp.noise(plan, out, w.C, w.sigma, w.noise_seed, 0, ws=ws)
     torch.cuda.synchronize()
-    launches = norm_launches(w, plan, dp) if phase == "norms" else None
+    launches = (norm_launches(w, plan, dp) if phase == "norms" else
+                sum_launches(w, plan, dp) if phase == "clipped_sum" else None)
     print(json.dumps({"mode": "kernel", "workload": w.name, "phase": phase, "sum_policy": args.sum,
                       "calls": args.warmup + args.steps, "launches_per_call": launches,
                       "algorithmic_bytes_per_call": work[phase][0],

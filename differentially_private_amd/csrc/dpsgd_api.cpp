@@ -679,24 +679,38 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
         return fail(DPSGD_ERR_INVALID_ARG, "too many norm partials");
     }
 
-    // split counts of the GEMM clipped sums: ~8192 wavefronts per launch for the tile
+    // split counts of the GEMM clipped sums: ~16384 wavefronts per launch for the tile
     // engine, >= 256 workgroups of 256 x 256 tiles (one per CU) for the dense kernels
-    int64_t waves = 0, dense_wgs = 0;
+    int64_t waves_mb[3] = {0, 0, 0}, layers_mb[3] = {0, 0, 0}, dense_wgs = 0;
     for (LayerPlan& lp : p->layers) {
         if (lp.sum_mode != DPSGD_SUM_GEMM) continue;
         // (segment plans keep every GEMM sum on the tile engine, which walks each record's rows)
         lp.dense = p->dtype == DPSGD_DTYPE_BF16 && lp.tiles.mb == 2 && !p->segments;
-        if (lp.dense)
+        if (lp.dense) {
             dense_wgs += ((lp.d_in + 255) / 256) * ((lp.d_out + 255) / 256);
-        else
-            waves += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
+        } else {
+            waves_mb[lp.tiles.mb] += (int64_t)lp.tiles.tiles_x * lp.tiles.tiles_y;
+            ++layers_mb[lp.tiles.mb];
+        }
+    }
+    // the tile-engine sums go out in launches of at most kMaxLaunchLayers layers of one MB, so the
+    // wavefronts that matter are those of one launch: the smallest launch sets the split count (the
+    // 7B-shaped LoRA plan's 256 layers go out as six launches of ~1,370 wavefronts: 13 splits;
+    // measured there 52.8 / 49.5 / 47.9 / 47.0 / 48.9 ms for 1 / 4 / 7 / 13 / 25 splits, the last
+    // paying for its partials in the reduce)
+    int64_t waves = 0;
+    for (int mb = 1; mb <= 2; ++mb) {
+        if (!layers_mb[mb]) continue;
+        const int64_t launches = (layers_mb[mb] + kMaxLaunchLayers - 1) / kMaxLaunchLayers;
+        const int64_t per = std::max<int64_t>(1, waves_mb[mb] / launches);
+        waves = waves ? std::min(waves, per) : per;
     }
     auto splits_for = [&](int64_t units, int64_t target) -> int {
         if (units <= 0) return 1;
         return (int)std::min<int64_t>(std::min<int64_t>(p->B, 64),
                                       std::max<int64_t>(1, (target + units - 1) / units));
     };
-    const int ns = splits_for(waves, 8192);
+    const int ns = splits_for(waves, 16384);
     const int nsd = splits_for(dense_wgs, 256);
     p->n_splits_max = ns;
     p->n_splits_dense_max = nsd;

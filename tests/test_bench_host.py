@@ -43,6 +43,23 @@ def test_headline_algorithmic_bytes():
     wg = bench.algorithmic_work(w, g, dp)
     assert wg["stored_write"] == 0 and wg["norms"][0] == inputs
     assert wg["clipped_sum"] == [inputs + 16_777_216 * 4, 2 * 256 * 512 * 16_777_216]
+    assert bench.sum_launches(w, g, dp) == 6      # the tile-engine sums: 256 layers, 48 a launch
+    assert bench.sum_launches(w, plan, dp) == 0   # STORED: no GEMM sum
+
+
+def test_sum_launches_dense_and_lora():
+    """The dense clipped sum takes at most 32 layers a launch, the tile engine 48 per MFMA row-block
+    group; the GEMM lines report their per-launch figures over these counts."""
+    w4 = datagen.workload(4)
+    p4 = dp.Plan(w4.layers, w4.dtype, w4.B, w4.T)
+    assert bench.sum_launches(w4, p4, dp) == 1    # four 4096 x 4096 bf16 layers
+    w2 = datagen.workload(2)
+    p2 = dp.Plan(w2.layers, w2.dtype, w2.B, w2.T, dp.PATH_AUTO, dp.SUM_GEMM)
+    assert bench.sum_launches(w2, p2, dp) == 1    # 48 fp32 LoRA layers
+    layers = tuple([(64, 64)] * 40 + [(64, 8)] * 50)
+    p = dp.Plan(layers, dp.DTYPE_BF16, 4, 32, dp.PATH_AUTO, dp.SUM_GEMM)
+    w = w4.with_(layers=layers, layer_names=tuple(str(i) for i in range(90)), B=4, T=32)
+    assert bench.sum_launches(w, p, dp) == 2 + 2  # 40 dense (32 a launch), 50 tile-engine (48)
 
 
 def test_workload2_algorithmic_bytes():
