@@ -71,6 +71,9 @@ CASES = [
     ("lora_f32_gemm", ((64, 8), (8, 64)), F32, 40, dp.PATH_AUTO, dp.SUM_GEMM),
     ("bf16_gram", ((48, 40), (40, 48)), BF16, 24, dp.PATH_AUTO, dp.SUM_GEMM),
     ("bf16_direct_stored", ((48, 40), (40, 48)), BF16, 24, dp.PATH_DIRECT, dp.SUM_STORED),
+    # gradient blocks of whole 128-wide tiles kept in store order, the partial last tile natural
+    ("bf16_direct_stored_wide", ((300, 8), (8, 300)), BF16, 24, dp.PATH_DIRECT, dp.SUM_STORED),
+    ("f32_direct_stored_wide", ((260, 12), (12, 260)), F32, 24, dp.PATH_DIRECT, dp.SUM_STORED),
     ("bf16_dense_gram", ((320, 272),), BF16, 48, dp.PATH_GRAM, dp.SUM_GEMM),
     ("f32_gram", ((96, 80),), F32, 33, dp.PATH_GRAM, dp.SUM_AUTO),
 ]

@@ -53,6 +53,14 @@ STORED_CASES = [_stored_case(i) for i in range(12)] + [
     dict(dtype=F32, layers=tuple((4, 8) if l % 3 else (5, 3) for l in range(50)), B=5, T=3,
          seed=9002),                                                          # two tail launches
     dict(dtype=BF16, layers=((768, 8), (8, 768), (1024, 8)), B=7, T=40, seed=9003),  # wide layers
+    # stored-block order: whole 128-wide tiles kept in store order and the partial last tile in
+    # natural order (wide dimension 300 or 260), rows moving (wide d_in) or, for bf16, 4-column
+    # chunks moving (wide d_out), two 16-row blocks (d 36), and widths whose d_out is not a
+    # multiple of 4 (natural order throughout)
+    dict(dtype=F32, layers=((300, 8), (8, 300), (260, 12), (12, 260), (384, 36), (36, 384), (130, 6),
+                            (6, 130)), B=6, T=20, seed=9004),
+    dict(dtype=BF16, layers=((300, 8), (8, 300), (260, 12), (12, 260), (384, 36), (36, 384), (130, 6),
+                             (6, 130)), B=6, T=40, seed=9005),
 ]
 
 
