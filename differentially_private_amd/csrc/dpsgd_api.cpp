@@ -99,7 +99,6 @@ struct dpsgd_plan {
     int n_splits_max;        // tile-engine GEMM sums
     int n_splits_dense_max;  // dense GEMM sums
     bool segments;           // variable-length records (DPSGD_PLAN_SEGMENTS)
-    int64_t stored_bytes;    // STORED gradient blocks of one physical batch
     int64_t status_off, parts_off, n_off, c_off, seg_off;
     int64_t ws_bytes;
 };
@@ -173,13 +172,12 @@ void set_wpb(DirectArgs& a) {
     for (int l = 0; l < a.n_layers; ++l) a.L[l].wg_x = (a.L[l].tiles_x + wpb - 1) / wpb;
 }
 
-// STORED gradient blocks are written with non-temporal stores when a physical batch's blocks are
-// far larger than the 256 MB last-level cache: they would only displace the inputs there, and
-// the read-write mix reaches HBM faster (the 7B-shaped LoRA batch's 17.2 GB: 50.7 against 52.2 ms
-// of norm kernel).  Smaller sets are left to the cache, from which the finalize reads part of them
-// back (403 MB per batch of the 1024-hidden LoRA workload: its finalize ran at half the speed
-// with streaming stores).
-constexpr int64_t kStreamStoreBytes = (int64_t)1 << 30;
+// STORED gradient blocks leave the norm kernel by non-temporal stores, each whole tile in store
+// order so that every instruction writes whole lines: against plain stores, the norm launch of a
+// 43-layer slice of the 7B-shaped LoRA batch (2.9 GB of blocks) ran 9.30 against 9.66 ms, the OPT-125M-shaped step (19 MB)
+// 61.8 against 63.4 us and the 1024-hidden LoRA step (403 MB per physical batch) 17.95 against
+// 17.98 ms.  (Before the store order, a non-temporal store wrote half lines, and plain stores were
+// the faster choice below 1 GiB of blocks.)
 
 int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* const* A,
              const void* const* G, void* ws, hipStream_t s) {
@@ -203,7 +201,6 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
             a.parts_stride = p->parts_total;
             a.parts = parts;
             a.seg = ws_seg(ws, p);
-            const int store_mode = store ? (p->stored_bytes > kStreamStoreBytes ? 2 : 1) : 0;
             for (int l = l0; l < l1; ++l) {
                 const LayerPlan& lp = p->layers[l];
                 if (!in_group(lp)) continue;
@@ -225,14 +222,14 @@ int do_norms(const dpsgd_plan* p, int64_t n_rec, int l0, int l1, const void* con
                 d.split_stride = 0;
                 if (++a.n_layers == per) {
                     set_wpb(a);
-                    hipError_t e = launch_norm_direct(a, p->dtype, mb, store_mode, s);
+                    hipError_t e = launch_norm_direct(a, p->dtype, mb, store, s);
                     if (e != hipSuccess) return hip_fail(e, "ghost_norm (direct) launch");
                     a.n_layers = 0;
                 }
             }
             if (a.n_layers) {
                 set_wpb(a);
-                hipError_t e = launch_norm_direct(a, p->dtype, mb, store_mode, s);
+                hipError_t e = launch_norm_direct(a, p->dtype, mb, store, s);
                 if (e != hipSuccess) return hip_fail(e, "ghost_norm (direct) launch");
             }
         }
@@ -730,13 +727,10 @@ int dpsgd_plan_create(const dpsgd_plan_desc* d, dpsgd_plan** out, size_t* ws_byt
     p->n_off = region(p->B, 4);
     p->c_off = region(p->B, 4);
     p->seg_off = region(p->segments ? p->B + 1 : 0, 8);
-    p->stored_bytes = 0;
     for (LayerPlan& lp : p->layers) {
         lp.smap = stored_map(p->dtype, lp);
-        if (lp.sum_mode == DPSGD_SUM_STORED) {
+        if (lp.sum_mode == DPSGD_SUM_STORED)
             lp.stored_off = region(p->B, lp.n_params * 4);
-            if (fits) p->stored_bytes += p->B * lp.n_params * 4;   // bounded by the checked offsets
-        }
         else if ((lp.dense ? nsd : ns) > 1)
             lp.split_off = region(lp.dense ? nsd : ns, lp.n_params * 4);
     }

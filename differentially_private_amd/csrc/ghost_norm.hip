@@ -21,8 +21,8 @@ namespace dpsgd {
 
 // fp32, MB = 1 (LoRA shapes): ask for at least 4 wavefronts per SIMD (the kernel
 // then fits 5 without spilling), so that a whole LoRA workload's tiles are
-// resident at once and no tail of late wavefronts is left.  STORE: 0 = norms only,
-// 1 = the gradient blocks written too, 2 = written with non-temporal stores.
+// resident at once and no tail of late wavefronts is left.  STORE: 0 = norms only, 1 = the
+// gradient blocks written too (non-temporal stores, whole tiles in store order).
 template <int DT, int MB, int STORE>
 __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_direct(DirectArgs args) {
     const DirectLayer& L = args.L[blockIdx.z];
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(128, (DT == kF32 && MB == 1) ? 4 : 1) void k_norm_d
         args.parts[rec * args.parts_stride + L.part_off + tile_y * L.tiles_x + tile_x] = s;
     if (STORE) {
         float* dst = L.P + rec * (int64_t)L.dX * L.dY;
-        direct_store<DT, MB, STORE == 2, true>(dst, L, n0, m0, g, c, acc, false);
+        direct_store<DT, MB, true, true>(dst, L, n0, m0, g, c, acc, false);
     }
 }
 
@@ -542,8 +542,7 @@ hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, int store,
 #define DPSGD_LAUNCH(DT, MB, ST) hipLaunchKernelGGL((k_norm_direct<DT, MB, ST>), grid, dim3(64 * a.wpb), 0, s, a)
 #define DPSGD_LAUNCH_ST(DT, MB)                          \
     do {                                                 \
-        if (store == 2) DPSGD_LAUNCH(DT, MB, 2);         \
-        else if (store == 1) DPSGD_LAUNCH(DT, MB, 1);    \
+        if (store) DPSGD_LAUNCH(DT, MB, 1);              \
         else DPSGD_LAUNCH(DT, MB, 0);                    \
     } while (0)
     if (dtype == kBF16) {

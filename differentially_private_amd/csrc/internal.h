@@ -218,7 +218,7 @@ static_assert(sizeof(DirectArgs) <= 4096 && sizeof(GramArgs) <= 4096 && sizeof(R
 constexpr int64_t kScratchBytes = (int64_t)64 << 20;
 
 // ---- launchers (return hipError_t of the launch) ----
-hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, int store, hipStream_t s);  // store: 0, 1, 2 = streaming
+hipError_t launch_norm_direct(const DirectArgs& a, int dtype, int mb, int store, hipStream_t s);  // store: write the blocks
 hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s);
 hipError_t launch_clip(const ClipArgs& a, hipStream_t s);
 hipError_t launch_sum_direct(const DirectArgs& a, int dtype, int mb, int n_splits, hipStream_t s);
