@@ -171,6 +171,12 @@ def _gemm_case(i):
 GEMM_CASES = [_gemm_case(i) for i in range(14)] + [
     dict(dtype=BF16, layers=((256, 128), (64, 512)), B=9, T=64, seed=9201, path=dp.PATH_DIRECT),  # copy kernel
     dict(dtype=BF16, layers=((200, 136),), B=13, T=50, seed=9202, path=dp.PATH_DIRECT),           # register kernel
+    # more layers than one launch takes: the record splits are chosen per launch (here 20 and 12,
+    # every split a single record), each launch followed by its split reduce
+    dict(dtype=F32, layers=tuple((64, 8) if l % 2 else (8, 64) for l in range(100)), B=20, T=16,
+         seed=9203, path=dp.PATH_DIRECT),                                                        # 3 launches
+    dict(dtype=BF16, layers=tuple((300, 12) if l % 2 else (12, 300) for l in range(60)) + ((64, 64),) * 3,
+         B=12, T=32, seed=9204, path=dp.PATH_DIRECT),                                            # 2 + dense
 ]
 
 
