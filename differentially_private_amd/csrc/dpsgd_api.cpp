@@ -1004,7 +1004,7 @@ int dpsgd_philox_raw(uint64_t seed, uint64_t step, uint64_t first_block, uint64_
 
 int64_t dpsgd_poisson_ws_bytes(int64_t population) {
     if (population < 0) return -1;
-    return std::max<int64_t>(16, 16 * sample_wgs(population));
+    return std::max<int64_t>(16, sample_ws_bytes(population));
 }
 
 int dpsgd_poisson_sample(uint64_t seed, uint64_t step, double q, int64_t population, uint8_t* mask,

@@ -241,8 +241,9 @@ double rdp_epsilon(const double* orders, const double* rdp, int n, double delta,
 double gaussian_pair_delta(double eps, double mu);
 double gaussian_pair_epsilon(double delta, double mu);
 
-// Poisson sampler: ws holds 2 * sample_wgs(n) int64
+// Poisson sampler: ws holds 2 * sample_wgs(n) int64 and the inclusion bits, sample_ws_bytes(n) in all
 int64_t sample_wgs(int64_t n);
+int64_t sample_ws_bytes(int64_t n);
 hipError_t launch_poisson_sample(uint64_t seed, uint64_t step, uint64_t thr, int64_t n, uint8_t* mask,
                                  int64_t* indices, int64_t* count, int64_t* ws, hipStream_t s);
 

@@ -29,7 +29,10 @@ def gpu_sample(seed, step, q, n, with_mask=True):
 @pytest.mark.parametrize("seed,step,q,n", [(0, 0, 0.01, 1_000_000), (7, 3, 0.5, 4097), (7, 4, 0.5, 4097),
                                            (2**64 - 1, 2**40, 0.25, 1023), (5, 1, 0.0, 5000),
                                            (5, 1, 1.0, 5001), (9, 9, 0.999, 3), (1, 2, 0.37, 0),
-                                           (11, 0, 0.03, 3_000_001)])
+                                           (11, 0, 0.03, 3_000_001),
+                                           # more workgroup counts than the scan has threads: each
+                                           # scan thread takes a run of them
+                                           (13, 2, 0.05, 5_000_001), (17, 8, 0.01, 2**25 + 3)])
 def test_sampler_matches_oracle(seed, step, q, n):
     print("sampler", seed, step, q, n, flush=True)
     idx, c, mask, raw = gpu_sample(seed, step, q, n)
