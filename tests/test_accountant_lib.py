@@ -90,4 +90,10 @@ def test_sampler_rejects_before_launch(kw):
                           a["ws"], mask=a["mask"], stream=0)
     assert e.value.code == dp.ERR_INVALID_ARG
     assert dp.poisson_ws_bytes(-1) == -1 and dp.poisson_ws_bytes(0) == 16
-    assert dp.poisson_ws_bytes(1024) == 16 and dp.poisson_ws_bytes(1025) == 32
+    # two int64 per workgroup of 8,192 records, then 4 bytes of inclusion bits per 32 records
+    # (rounded up to 8 bytes)
+    def ws(n):
+        return 16 * -(-n // 8192) + 8 * -(-(-(-n // 32) * 4) // 8)
+    for n in (1, 31, 32, 33, 1024, 1025, 8192, 8193, 1 << 27, (1 << 36)):
+        assert dp.poisson_ws_bytes(n) == ws(n), n
+    assert dp.poisson_ws_bytes(1024) == 144 and dp.poisson_ws_bytes(8193) == 1064
