@@ -606,15 +606,30 @@ def users_line(args, w, torch, dev, dp, datagen):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
+    # the norm phase alone, its C call's arguments marshalled once so that the host does not pace it
+    lib = dp.load()
+    pa, pg, wsp, sp = dp._ptr_array(As), dp._ptr_array(Gs), ws.data_ptr(), stream.cuda_stream
     x0, x1 = ev(), ev()
     x0.record(stream)
     for _ in range(args.steps):
-        dp.norms(plan, n_users, 0, w.n_layers, As, Gs, ws)
+        rc = lib.dpsgd_norms(plan.handle, n_users, 0, w.n_layers, pa, pg, wsp, sp)
+        if rc:
+            dp._check(rc)
     x1.record(stream)
     torch.cuda.synchronize()
     norm_ms = x0.elapsed_time(x1) / args.steps
     rows = int(offs[-1])
-    norm_bytes = rows * sum(di + do for di, do in w.layers) * 4 + n_users * w.n_params * 4
+    in_bytes = rows * sum(di + do for di, do in w.layers) * 4          # A and G read once
+    gbs = in_bytes / (norm_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None, "kernel": "k_norm_direct (ghost_norm, direct path, segment plan)",
+            "phase": "norms", "launches_per_phase": 1, "algorithmic_bytes_per_launch": in_bytes,
+            "avg_ms": norm_ms,
+            "stored_gradient_blocks": {"bytes_written": n_users * w.n_params * 4,
+                                       "bytes_read": n_users * w.n_params * 4,
+                                       "note": "each user's gradient block, written by the norm kernel "
+                                               "and read back by the fused sum + noise kernel; not "
+                                               "algorithmic bytes"}}
     line = {"metric": "users/sec per DP-SGD step with user-level clipping", "value": n_users / (ms * 1e-3),
             "unit": "users/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -623,10 +638,37 @@ def users_line(args, w, torch, dev, dp, datagen):
                        "token_rows": rows, "max_rows_per_user": T_max, "layers": w.n_layers,
                        "params": w.n_params, "parallelism": "single GPU"},
             "phases_ms": {"norms": norm_ms, "rest_of_step": ms - norm_ms},
-            "norms_roofline": {"hbm_GBps": norm_bytes / (norm_ms * 1e-3) / 1e9,
-                               "hbm_frac": norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "algorithmic_bytes": norm_bytes}}
+            "roofline": roof,
+            "cpu_baseline": None if args.no_cpu_baseline else users_cpu_baseline(w, recs, args.cpu_seconds)}
     print(json.dumps(line), flush=True)
+
+
+def users_cpu_baseline(w, recs, seconds):
+    """The oracle on the same users: each user's records' rows concatenated into one record of its own
+    length (the oracle's gradient rows sum over them), one oracle step per user, all layers, repeated
+    for about `seconds` on the host's threads; users/s."""
+    import datagen
+    import oracle
+    cores = oracle.num_threads()
+    users, first = [], 0
+    for r in recs:
+        A = [datagen.host_tensor(w, l, 0, first, r).reshape(1, r * w.T, -1) for l in range(w.n_layers)]
+        G = [datagen.host_tensor(w, l, 1, first, r).reshape(1, r * w.T, -1) for l in range(w.n_layers)]
+        users.append((A, G))
+        first += r
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for A, G in users:
+            oracle.step(A, G, w.C, w.sigma, w.noise_seed, 0)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": len(recs) * reps / el, "unit": "users/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x all {len(recs)} users ({sum(recs)} records of {w.T} tokens) over all "
+                      f"{w.n_layers} layers, one oracle step per user on its concatenated rows (its noise "
+                      f"over all {w.n_params} parameters included); input generation excluded; "
+                      f"{el:.1f} s wall"}
 
 
 I8_PEAK_TOPS = 5000.0   # dense INT8 MFMA, ops/s x 1e-12
