@@ -570,6 +570,15 @@ def sample_line(args, torch, dev, dp):
             "dtype": "u32", "data": "synthetic",
             "config": {"workload": "poisson_sampler", "population": n, "q": q, "selected_last": sel},
             "bytes_written_GBps": (n + 8 * sel) / (ms * 1e-3) / 1e9,
+            "roofline": {"bound": "alu", "achieved": SAMPLE_OPS_PER_RECORD * n / (ms * 1e-3) / 1e12,
+                         "peak": VALU_PEAK_TOPS, "unit": "T lane-ops/s",
+                         "frac": SAMPLE_OPS_PER_RECORD * n / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
+                         "traffic": None,
+                         "kernel": "k_sample_count + k_sample_scan + k_sample_write (one draw)",
+                         "algorithmic_ops_per_launch": SAMPLE_OPS_PER_RECORD * n, "avg_ms": ms,
+                         "how": "Philox4x32-10 per 4 records: 10 rounds of two 32x32->64-bit products "
+                                "and two XORs; one comparison per record; against the 32-bit VALU "
+                                "lane-op rate, the draw's three launches timed together"},
             "cpu_baseline": {"value": cpu_rate, "unit": "records/s", "cores": 1, "kind": "oracle",
                              "sample": f"{m} records, one draw"},
             "accountant": {"epsilon_300_steps": eps, "order": order, "host_ms": host_ms}}
@@ -672,6 +681,12 @@ def users_cpu_baseline(w, recs, seconds):
 
 
 I8_PEAK_TOPS = 5000.0   # dense INT8 MFMA, ops/s x 1e-12
+# 32-bit VALU lane operations per second x 1e-12: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (the vendor's
+# 157.3 TFLOP/s fp32 vector figure is this rate x 2 for a fused multiply-add x 2 for packed pairs)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# the sampler's algorithmic 32-bit operations per record: Philox4x32-10 serves four records with
+# 10 rounds of two 32x32->64-bit products and two XORs (40 / 4), plus one comparison
+SAMPLE_OPS_PER_RECORD = 11
 
 
 def int8_model(torch, dev, dp, seed=0):
