@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t draw4(uint64_t seed, uint64_t step, uint64_t
     return bits;
 }
 
+// draw4 for a block whose four records all exist, with the threshold as thr - 1 (thr >= 1): a
+// word w is included iff w <= thr - 1, a 32-bit compare even for thr = 2^32 (q = 1)
+__device__ __forceinline__ uint32_t draw4_full(uint64_t seed, uint64_t step, uint32_t thr_m1, int64_t b) {
+    const Philox4 w = philox4x32_10((uint64_t)b | (1ull << 63), step, seed);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bits |= (uint32_t)(w.x[k] <= thr_m1) << k;
+    return bits;
+}
+
 // inclusive prefix sum of v over the wavefront
 template <typename V>
 __device__ __forceinline__ V wave_prefix(V v, int lane) {
@@ -60,10 +70,19 @@ __global__ __launch_bounds__(kThreads) void k_sample_count(uint64_t seed, uint64
     __shared__ int wsum[kThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t g = (int64_t)blockIdx.x * kThreads + tid;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < kBlocksPerThread; ++j) bits |= draw4(seed, step, thr, kBlocksPerThread * g + j, n) << (4 * j);
     const int64_t r0 = kPerThread * g;
+    uint32_t bits = 0;
+    if (thr != 0 && r0 + kPerThread <= n) {
+        // all 32 records exist: no per-record bounds, 32-bit compares
+        const uint32_t thr_m1 = (uint32_t)(thr - 1);
+#pragma unroll
+        for (int j = 0; j < kBlocksPerThread; ++j)
+            bits |= draw4_full(seed, step, thr_m1, kBlocksPerThread * g + j) << (4 * j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kBlocksPerThread; ++j)
+            bits |= draw4(seed, step, thr, kBlocksPerThread * g + j, n) << (4 * j);
+    }
     if (r0 < n) {
         bitsw[g] = bits;
         if (mask) {
