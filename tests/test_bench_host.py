@@ -100,3 +100,12 @@ def test_traffic_records_follow_the_sources(path, names, tmp_path):
         data = open(os.path.join(ROOT, "differentially_private_amd", "csrc", n), "rb").read()
         altered.update(data + (b" " if i == len(names) - 1 else b""))
     assert altered.hexdigest()[:16] != h
+
+
+@pytest.mark.parametrize("path,names", _traffic_records())
+def test_traffic_records_are_current(path, names):
+    """The committed counter records were taken on the sources as they stand: an edit of a hashed
+    source without new counters would leave the bench lines' `traffic` null."""
+    rec = json.load(open(os.path.join(ROOT, "profiles", path)))
+    assert rec["src_hash"] == bench.kernel_src_hash(names), \
+        f"{path}: its counters predate the current sources; take FETCH_SIZE / WRITE_SIZE again"
