@@ -156,6 +156,16 @@ __device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t
         : "memory", "m0");
 }
 
+// copy16 with the non-temporal (streaming) cache policy, for bytes that are read once
+__device__ __forceinline__ void copy16_nt(const char* base, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(min(later, 3) * PER): wait until at most the `later` most recently issued
 // k-steps of PER copies each are still in flight (copies complete in issue order).
 template <int PER>

@@ -14,6 +14,7 @@
 // Each wavefront writes one fp32 partial per (record, tile): the partials of a
 // record depend only on that record's rows, so the norms are batch-invariant.
 #include <algorithm>
+#include <type_traits>
 
 #include "tile_direct.h"
 
@@ -326,26 +327,39 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
 // Same inputs as k_norm_gram_copy (bf16, 16-byte aligned rows, d_in and d_out multiples
 // of 32), with the nb (nb + 1) / 2 upper-triangle pairs of 64-token blocks of one
 // (record, layer) in a single workgroup, so each token row is copied into LDS once per
-// feature step rather than once per block pair it belongs to, and the copies run up to
-// 7 steps ahead (stages of all 4 nb 16-row blocks, 4 nb KB each, as many as fit in
-// 144 KB, at most 8).  Wavefronts:
+// feature step rather than once per block pair it belongs to.  A feature step is 64 features,
+// one whole 128-byte line of every token row: each copy instruction moves 8 rows x 128 bytes,
+// so no line is fetched from HBM in two halves at different times (64-byte pieces of 8 KB rows,
+// the 32-feature steps of the pair kernel, stream at about 70% of the rate of whole lines), and
+// the copies take the non-temporal policy, since every byte is read once.  The last step of A
+// or G is a half step when the width is an odd multiple of 32.
+// Wavefronts:
 //  - one per off-diagonal pair (tb < sb): the full 64 x 64 Gram blocks of A and G,
 //    formed exactly as a k_norm_gram_copy wavefront forms them;
 //  - one per two diagonal blocks: only the 10 upper-triangle 16 x 16 tiles of each
 //    64 x 64 diagonal block (the Gram is symmetric), the strictly upper ones doubled in
 //    the Hadamard sum.
 // For nb = 4 that is 6 + 2 = 8 wavefronts, two per SIMD.  Each wavefront issues the
-// same number of 1 KB copies per step (blocks w * per + j mod 4 nb; a block may be copied
-// twice, with the same bytes to the same place), so one vmcnt value describes every
+// same number of 1 KB copies per step (half-blocks w * per + j mod 8 nb; a half-block may be
+// copied twice, with the same bytes to the same place), so one vmcnt value describes every
 // wavefront's copies in flight.  Partials go to the slots k_norm_gram uses.
+//
+// Stage layout: 16-row block b at 2 KB * b, its rows 0-7 in the first KB and 8-15 in the
+// second, 128 bytes per row; logical 16-byte chunk j of row r (8 features) sits at chunk
+// j ^ rec_swz(r).  An MFMA operand read (lane 16 g + c: row c, chunk 4 q + g for the q-th 32
+// features of the step) then puts the 16 rows of each 16-lane group on 16 distinct 16-byte
+// bank slots (rows of one parity differ in r >> 1).  The copies write LDS linearly by lane,
+// so the swizzle is applied to the source chunk, inside the same 128-byte line.
 constexpr int kGramRecMaxNb = 4;                 // T <= 256
 constexpr int kGramRecWaves = 8;                 // for nb = 4
+constexpr int kGramRecK = 64;                    // features per step
 constexpr int kGramRecMaxLds = 144 * 1024;
 constexpr int kGramRecMaxStages = 8;
-// a group of two steps needs both copied before the previous group's barrier: 4 stages or more
-static_assert(kGramRecMaxLds / (4 * kGramRecMaxNb * 1024) >= 4 && kGramRecMaxStages >= 4, "stages");
+static_assert(kGramRecMaxLds / (8 * kGramRecMaxNb * 1024) >= 2, "stages");
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 28]
+__device__ __forceinline__ int rec_swz(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63]
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
 #define DPSGD_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
@@ -353,6 +367,11 @@ __device__ __forceinline__ void wait_vm(int n) {
         DPSGD_VM(8) DPSGD_VM(9) DPSGD_VM(10) DPSGD_VM(11) DPSGD_VM(12) DPSGD_VM(13) DPSGD_VM(14)
         DPSGD_VM(15) DPSGD_VM(16) DPSGD_VM(17) DPSGD_VM(18) DPSGD_VM(19) DPSGD_VM(20) DPSGD_VM(21)
         DPSGD_VM(22) DPSGD_VM(23) DPSGD_VM(24) DPSGD_VM(25) DPSGD_VM(26) DPSGD_VM(27) DPSGD_VM(28)
+        DPSGD_VM(29) DPSGD_VM(30) DPSGD_VM(31) DPSGD_VM(32) DPSGD_VM(33) DPSGD_VM(34) DPSGD_VM(35)
+        DPSGD_VM(36) DPSGD_VM(37) DPSGD_VM(38) DPSGD_VM(39) DPSGD_VM(40) DPSGD_VM(41) DPSGD_VM(42)
+        DPSGD_VM(43) DPSGD_VM(44) DPSGD_VM(45) DPSGD_VM(46) DPSGD_VM(47) DPSGD_VM(48) DPSGD_VM(49)
+        DPSGD_VM(50) DPSGD_VM(51) DPSGD_VM(52) DPSGD_VM(53) DPSGD_VM(54) DPSGD_VM(55) DPSGD_VM(56)
+        DPSGD_VM(57) DPSGD_VM(58) DPSGD_VM(59) DPSGD_VM(60) DPSGD_VM(61) DPSGD_VM(62) DPSGD_VM(63)
 #undef DPSGD_VM
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
@@ -361,6 +380,9 @@ __device__ __forceinline__ void wait_vm(int n) {
 // upper-triangle 16 x 16 tile (mi <= ni) of a 64 x 64 diagonal block -> 0..9
 __host__ __device__ constexpr int tri_tile(int mi, int ni) { return mi * 4 - mi * (mi - 1) / 2 + (ni - mi); }
 
+template <int N>
+using Subs = std::integral_constant<int, N>;
+
 __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs args, int n_stages) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds_rec[];
     const GramLayer& L = args.L[blockIdx.y];
@@ -368,8 +390,8 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
     const int64_t T = args.T;
     const int nb = args.nb;                 // 64-token blocks (1..4)
     const int n_off = nb * (nb - 1) / 2;    // off-diagonal pairs: waves 0 .. n_off - 1
-    const int n16 = 4 * nb;                 // 16-row blocks per stage (rows past T repeat row T - 1)
-    const int stage_elems = n16 * 512;      // 1 KB per 16-row block
+    const int n8 = 8 * nb;                  // 8-row half-blocks per stage (rows past T repeat row T - 1)
+    const int stage_elems = n8 * 512;       // 1 KB per half-block
     const int nw = (int)(blockDim.x >> 6);  // n_off + ceil(nb / 2)
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -389,20 +411,32 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
     const int d0 = 2 * (w - n_off);
     const bool has_d1 = !off_wave && d0 + 1 < nb;
 
-    // copies: wave w issues blocks (w * per + j) mod n16, j < per; lane L fetches chunk L / 16
-    // of row L % 16 of the block (row clamped to T - 1)
-    const int per = (n16 + nw - 1) / nw;    // 1 .. 4
-    uint32_t offa[4], offg[4], dsto[4];
+    // copies: wave w issues half-blocks h = (w * per + j) mod n8, j < per; lane L fetches
+    // physical chunk L % 8 of row 8 (h % 2) + L / 8 of block h / 2 (token row clamped to T - 1),
+    // i.e. logical chunk (L % 8) ^ rec_swz(row); a half step reads chunk (logical & 3) instead,
+    // inside the row, and those LDS chunks are never read.
+    const int per = (n8 + nw - 1) / nw;     // 4 .. 8
+    // Half-block h of a step holds token rows 8 h .. 8 h + 7 (rows 8 e .. 8 e + 7 of 16-row block
+    // h / 2, e = h % 2); this lane copies row 8 h + lane / 8 (clamped to T - 1), logical chunk
+    // (lane % 8) ^ rec_swz(8 e + lane / 8).  A wave's j-th copy has parity e = (w per + j) % 2 (8 nb
+    // is even), so the lane's part of the source offset is one of two values per tensor, indexed
+    // by j % 2; the rows' part, 16 h d bytes, goes into the scalar base.
+    const int tlast = (int)T - 1;           // T <= 256 here
+    int hs[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int b = (w * per + j) % n16;
-        int64_t t = 16 * (int64_t)b + (lane & 15);
-        if (t > T - 1) t = T - 1;
-        offa[j] = (uint32_t)((t * L.d_in + 8 * (lane >> 4)) * 2);
-        offg[j] = (uint32_t)((t * L.d_out + 8 * (lane >> 4)) * 2);
-        dsto[j] = (uint32_t)(b * 1024);
+    for (int j = 0; j < 8; ++j) hs[j] = (w * per + j) % n8;
+    int jls[2];
+    uint32_t vA[2], vG[2], hi4[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int par = (w * per + e) & 1;
+        jls[e] = (lane & 7) ^ rec_swz(8 * par + (lane >> 3));
+        vA[e] = (uint32_t)(lane >> 3) * (uint32_t)L.d_in * 2u + 16u * (uint32_t)jls[e];
+        vG[e] = (uint32_t)(lane >> 3) * (uint32_t)L.d_out * 2u + 16u * (uint32_t)jls[e];
+        hi4[e] = 16u * (uint32_t)(jls[e] & 4);   // a half step reads logical chunk j & 3
     }
-    const int nA = L.d_in / kGramK, nG = L.d_out / kGramK;
+    const int nA = (L.d_in + kGramRecK - 1) / kGramRecK, nG = (L.d_out + kGramRecK - 1) / kGramRecK;
+    const bool halfA = L.d_in % kGramRecK != 0, halfG = L.d_out % kGramRecK != 0;
     const int total = nA + nG;
     const char* recA = static_cast<const char*>(L.A) + rec * T * L.d_in * 2;
     const char* recG = static_cast<const char*>(L.G) + rec * T * L.d_out * 2;
@@ -410,35 +444,50 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
     auto issue = [&](int s, int st) {
         const uint32_t dst = lds0 + (uint32_t)(st * stage_elems * 2);
         const bool a_step = s < nA;
-        const char* base = a_step ? recA + (int64_t)s * kGramK * 2 : recG + (int64_t)(s - nA) * kGramK * 2;
+        const char* base = a_step ? recA + (int64_t)s * kGramRecK * 2 : recG + (int64_t)(s - nA) * kGramRecK * 2;
+        const bool half = a_step ? (halfA && s == nA - 1) : (halfG && s == total - 1);
+        const uint32_t d = (uint32_t)(a_step ? L.d_in : L.d_out);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (j < per) copy16(base, a_step ? offa[j] : offg[j], dst + dsto[j]);
+        for (int j = 0; j < 8; ++j)
+            if (j < per) {
+                const int h = hs[j];
+                if (8 * h + 7 <= tlast) {
+                    const uint32_t off = (a_step ? vA[j & 1] : vG[j & 1]) - (half ? hi4[j & 1] : 0u);
+                    copy16_nt(base + (int64_t)h * 16 * d, off, dst + (uint32_t)h * 1024u);
+                } else {
+                    const int t = min(8 * h + (lane >> 3), tlast);
+                    const int jl = half ? (jls[j & 1] & 3) : jls[j & 1];
+                    copy16_nt(base, (uint32_t)t * d * 2u + 16u * (uint32_t)jl, dst + (uint32_t)h * 1024u);
+                }
+            }
     };
+    // operand offsets (elements, within a 16-row block) of this lane's row c, logical chunk
+    // 4 q + g, for the two 32-feature halves q of a step
+    int lofs[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lofs[q] = 512 * (c >> 3) + 64 * (c & 7) + 8 * ((4 * q + g) ^ rec_swz(c));
 
-    // The copy pipeline: feature steps in groups of two (one at the end of a phase) per barrier,
-    // the A steps then the G steps, so that within a group the second step's LDS reads can
-    // overlap the first step's MFMAs.  At a group's barrier every earlier step is retired and
-    // its stage is refilled with the next step to copy.  Each role runs its own copy of the
-    // loop so that its accumulators live only there; both pass the same barriers.
+    // The copy pipeline: one feature step per barrier, the A steps then the G steps.  At step
+    // s's barrier step s is copied and step s - 1 is retired, and its stage is refilled with the
+    // next step to copy (n_stages - 1 steps ahead).  Each role runs its own copy of the loop so
+    // that its accumulators live only there; both pass the same barriers.
     const int n = n_stages;
     auto pipeline = [&](auto&& step_a, auto&& step_g) {
         int next = min(n, total);   // next step to copy
         for (int k = 0; k < next; ++k) issue(k, k);
         int s = 0;
-        auto group = [&](int m, auto&& compute) {
-            wait_vm(per * (next - s - m));   // steps s .. s + m - 1 done, later ones in flight
+        auto begin = [&]() -> const uint16_t* {
+            wait_vm(per * (next - s - 1));   // step s done, later ones in flight
             __syncthreads();
             const int lim = min(total, s + n);
             for (; next < lim; ++next) issue(next, next % n);
-            compute();
-            s += m;
+            return lds_rec + (s % n) * stage_elems;
         };
-        auto stage = [&](int k) { return lds_rec + (k % n) * stage_elems; };
-        while (s + 1 < nA) group(2, [&] { step_a(stage(s)); step_a(stage(s + 1)); });
-        if (s < nA) group(1, [&] { step_a(stage(s)); });
-        while (s + 1 < total) group(2, [&] { step_g(stage(s)); step_g(stage(s + 1)); });
-        if (s < total) group(1, [&] { step_g(stage(s)); });
+        // one loop per phase and kind of step, so that each loop touches one accumulator set
+        for (const int e = nA - (halfA ? 1 : 0); s < e; ++s) step_a(begin(), Subs<2>{});
+        if (halfA) step_a(begin(), Subs<1>{}), ++s;
+        for (const int e = total - (halfG ? 1 : 0); s < e; ++s) step_g(begin(), Subs<2>{});
+        if (halfG) step_g(begin(), Subs<1>{}), ++s;
     };
     float* parts = args.parts + rec * args.parts_stride + L.part_off;
 
@@ -450,20 +499,28 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
             ga[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             gg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        auto step = [&](const uint16_t* S, f32x4 (&acc)[16]) {
-            u32x4 av[4], bv[4];
+        auto step = [&](const uint16_t* S, f32x4 (&acc)[16], auto subs) {
+            constexpr int NQ = decltype(subs)::value;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * tb + mi) * 512 + 8 * lane);
+            for (int q = 0; q < NQ; ++q) {
+                u32x4 av[4], bv[4];
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                bv[ni] = *reinterpret_cast<const u32x4*>(S + (4 * sb + ni) * 512 + 8 * lane);
+                for (int mi = 0; mi < 4; ++mi)
+                    av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * tb + mi) * 1024 + lofs[q]);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+                for (int ni = 0; ni < 4; ++ni)
+                    bv[ni] = *reinterpret_cast<const u32x4*>(S + (4 * sb + ni) * 1024 + lofs[q]);
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) acc[4 * mi + ni] = mfma_bf16(av[mi], bv[ni], acc[4 * mi + ni]);
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        acc[4 * mi + ni] = mfma_bf16(av[mi], bv[ni], acc[4 * mi + ni]);
+                // the next half's operand reads follow these MFMAs (and overlap their execution)
+                if (q + 1 < NQ) __builtin_amdgcn_sched_barrier(0);
+            }
         };
-        pipeline([&](const uint16_t* S) { step(S, ga); }, [&](const uint16_t* S) { step(S, gg); });
+        pipeline([&](const uint16_t* S, auto subs) { step(S, ga, subs); },
+                 [&](const uint16_t* S, auto subs) { step(S, gg, subs); });
         float sum = 0.f;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -488,24 +545,30 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
             da[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             dg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        auto step = [&](const uint16_t* S, f32x4 (&acc)[20]) {
-            u32x4 av[2][4];
+        auto step = [&](const uint16_t* S, f32x4 (&acc)[20], auto subs) {
+            constexpr int NQ = decltype(subs)::value;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                av[0][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d0 + mi) * 512 + 8 * lane);
-                av[1][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d1 + mi) * 512 + 8 * lane);
+            for (int q = 0; q < NQ; ++q) {
+                u32x4 av[2][4];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    av[0][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d0 + mi) * 1024 + lofs[q]);
+                    av[1][mi] = *reinterpret_cast<const u32x4*>(S + (4 * d1 + mi) * 1024 + lofs[q]);
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                        for (int ni = mi; ni < 4; ++ni) {
+                            const int k = 10 * e + tri_tile(mi, ni);
+                            acc[k] = mfma_bf16(av[e][mi], av[e][ni], acc[k]);
+                        }
+                if (q + 1 < NQ) __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = mi; ni < 4; ++ni) {
-                        const int q = 10 * e + tri_tile(mi, ni);
-                        acc[q] = mfma_bf16(av[e][mi], av[e][ni], acc[q]);
-                    }
         };
-        pipeline([&](const uint16_t* S) { step(S, da); }, [&](const uint16_t* S) { step(S, dg); });
+        pipeline([&](const uint16_t* S, auto subs) { step(S, da, subs); },
+                 [&](const uint16_t* S, auto subs) { step(S, dg, subs); });
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             if (e == 1 && !has_d1) break;
@@ -567,8 +630,8 @@ hipError_t launch_norm_gram(const GramArgs& a, int dtype, hipStream_t s) {
                a.T * (int64_t)std::max(d.d_in, d.d_out) * 2 < ((int64_t)1 << 31);
     }
     if (copy && a.nb <= kGramRecMaxNb) {
-        const int n_stages = std::min(kGramRecMaxStages, kGramRecMaxLds / (4 * a.nb * 1024));
-        const size_t lds = (size_t)n_stages * 4 * a.nb * 1024;
+        const int n_stages = std::min(kGramRecMaxStages, kGramRecMaxLds / (8 * a.nb * 1024));
+        const size_t lds = (size_t)n_stages * 8 * a.nb * 1024;
         const int nw = a.nb * (a.nb - 1) / 2 + (a.nb + 1) / 2;
         hipLaunchKernelGGL(k_norm_gram_rec, dim3((unsigned)a.n_rec, a.n_layers), dim3(64 * nw), lds, s, a,
                            n_stages);
