@@ -188,16 +188,28 @@ __global__ __launch_bounds__(256) void k_norm_gram(GramArgs args) {
 // features, then the sum of their Hadamard product, doubled off the diagonal.  In a diagonal
 // workgroup wave (1, 0) holds the mirror image of wave (0, 1)'s sub-pair and writes nothing.
 //
-// Features stream in k-steps of 32 through one copy pipeline, first A's d_in features, then G's
-// d_out: per k-step the 128 I rows and 128 J rows (16 blocks of 16 rows, 16 KB) are copied by
-// global_load_lds_dwordx4 into 3 LDS stages, two k-steps ahead, one barrier per k-step.  Each
-// 16-row block is stored chunk-major (8-feature chunk k of row r at byte 256 k + 16 r), so an
-// MFMA operand read (lane 16 g + c: row c, chunk g) is one linear 16-byte-per-lane LDS read.
-// Token rows past T are copied from row T - 1 and left out of the Hadamard sum.
+// Features stream in steps of 64 through one copy pipeline, first A's d_in features, then G's
+// d_out: per step the 128 I rows and 128 J rows (16 blocks of 16 rows, 32 KB) are copied by
+// global_load_lds_dwordx4 with the non-temporal policy into 2 LDS stages, one step ahead, one
+// barrier per step.  Each copy instruction moves 8 rows x 128 bytes, whole lines (64-byte pieces
+// of long rows stream at about 70% of the rate of whole lines).  Stage layout: 16-row block b at
+// 2 KB * b, rows 0-7 in its first KB and 8-15 in its second, 128 bytes per row, logical 16-byte
+// chunk j of row r at chunk j ^ row_swz(r), so that the 16 rows of an MFMA operand read (lane
+// 16 g + c: row c, chunk 4 q + g for the q-th 32 features of the step) fall on 16 distinct
+// 16-byte bank slots; the copies write LDS linearly by lane, so the swizzle is applied to the
+// source chunk, inside the same line.  A width that is an odd multiple of 32 ends with a half
+// step.  Token rows past T are copied from row T - 1 and left out of the Hadamard sum.
 constexpr int kGramB = 128;                   // tokens per block
-constexpr int kGramK = 32;                    // features per k-step
-constexpr int kGramStages = 3;
-constexpr int kGramStage = 2 * kGramB * kGramK * 2;   // 16 KB: I rows, then J rows
+constexpr int kGramK = 32;                    // feature granularity of the Gram copy kernels
+constexpr int kGramCK = 64;                   // features per step
+constexpr int kGramStages = 2;
+constexpr int kGramStage = 2 * kGramB * kGramCK * 2;   // 32 KB: I rows, then J rows
+
+__device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 7; }
+
+// a step of NQ 32-feature halves (2, or 1 for a half step)
+template <int N>
+using Subs = std::integral_constant<int, N>;
 
 __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[kGramStages * kGramStage / 2];
@@ -207,9 +219,9 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
     // workgroup -> (record, pair): workgroup ids go round-robin over the 8 XCDs and the pairs
     // of one record get ids equal mod 8, so they share an XCD's L2
     const int x = blockIdx.x;
-    const int q = x >> 3;
-    const int pair = q % np;
-    const int64_t rec = 8 * (int64_t)(q / np) + (x & 7);
+    const int q8 = x >> 3;
+    const int pair = q8 % np;
+    const int64_t rec = 8 * (int64_t)(q8 / np) + (x & 7);
     if (rec >= args.n_rec) return;
     int I = 0, rem = pair;
     while (rem >= nb - I) {
@@ -227,34 +239,48 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
     const bool mirror = (I == J) && wm > wn;
     const bool active = !mirror && tb < args.nb && sb < args.nb;
 
-    // copies: blocks 0..7 are I rows 16 b .., blocks 8..15 J rows; wave w issues blocks 4w .. 4w+3;
-    // lane L fetches chunk L / 16 of row L % 16 (row clamped to T - 1)
-    uint32_t offa[4], offg[4];   // byte offsets from the record's row 0 at the k-step's features
+    // copies: half-blocks 0..15 are I rows 8 h .., 16..31 J rows 8 (h - 16) ..; wave w issues
+    // half-blocks 8 w .. 8 w + 7 (half-block h is 16-row block h / 2, rows 8 (h % 2) ..); lane L
+    // fetches physical chunk L % 8 of row L / 8 of the half-block, i.e. logical chunk
+    // (L % 8) ^ row_swz(8 (h % 2) + L / 8), the row clamped to T - 1
+    uint32_t offa[8], offg[8];   // byte offsets from the record's row 0 at the step's features
+    uint32_t hi4[2];             // what a half step takes off (logical chunk j -> j & 3)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int b = 4 * w + k;
-        int64_t t = (b < 8 ? (int64_t)I * kGramB + 16 * b : (int64_t)J * kGramB + 16 * (b - 8)) + (lane & 15);
+    for (int e = 0; e < 2; ++e) hi4[e] = 16u * (uint32_t)((((lane & 7) ^ row_swz(8 * e + (lane >> 3)))) & 4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int h = 8 * w + k;
+        const int jl = (lane & 7) ^ row_swz(8 * (h & 1) + (lane >> 3));
+        int64_t t = (h < 16 ? (int64_t)I * kGramB + 8 * h : (int64_t)J * kGramB + 8 * (h - 16)) + (lane >> 3);
         if (t > T - 1) t = T - 1;
-        offa[k] = (uint32_t)((t * L.d_in + 8 * (lane >> 4)) * 2);
-        offg[k] = (uint32_t)((t * L.d_out + 8 * (lane >> 4)) * 2);
+        offa[k] = (uint32_t)((t * L.d_in + 8 * jl) * 2);
+        offg[k] = (uint32_t)((t * L.d_out + 8 * jl) * 2);
     }
-    const int nA = L.d_in / kGramK, nG = L.d_out / kGramK;
+    const int nA = (L.d_in + kGramCK - 1) / kGramCK, nG = (L.d_out + kGramCK - 1) / kGramCK;
+    const bool halfA = L.d_in % kGramCK != 0, halfG = L.d_out % kGramCK != 0;
     const int total = nA + nG;
     const char* recA = static_cast<const char*>(L.A) + rec * T * L.d_in * 2;
     const char* recG = static_cast<const char*>(L.G) + rec * T * L.d_out * 2;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
     auto issue = [&](int s, int st) {
-        const uint32_t dst = lds0 + (uint32_t)(st * kGramStage + 4 * w * 1024);
+        const uint32_t dst = lds0 + (uint32_t)(st * kGramStage + 8 * w * 1024);
         if (s < nA) {
-            const char* base = recA + (int64_t)s * kGramK * 2;
+            const char* base = recA + (int64_t)s * kGramCK * 2;
+            const bool half = halfA && s == nA - 1;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) copy16(base, offa[k], dst + k * 1024);
+            for (int k = 0; k < 8; ++k) copy16_nt(base, offa[k] - (half ? hi4[k & 1] : 0u), dst + k * 1024);
         } else {
-            const char* base = recG + (int64_t)(s - nA) * kGramK * 2;
+            const char* base = recG + (int64_t)(s - nA) * kGramCK * 2;
+            const bool half = halfG && s == total - 1;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) copy16(base, offg[k], dst + k * 1024);
+            for (int k = 0; k < 8; ++k) copy16_nt(base, offg[k] - (half ? hi4[k & 1] : 0u), dst + k * 1024);
         }
     };
+    // operand offsets (elements, within a 16-row block) of this lane's row c, logical chunk
+    // 4 q + g, for the two 32-feature halves q of a step
+    int lofs[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lofs[q] = 512 * (c >> 3) + 64 * (c & 7) + 8 * ((4 * q + g) ^ row_swz(c));
 
     f32x4 ga[4][4], gg[4][4];
 #pragma unroll
@@ -265,39 +291,56 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
             gg[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
+    auto step = [&](const uint16_t* S, f32x4 (&acc)[4][4], auto subs) {
+        constexpr int NQ = decltype(subs)::value;
 #pragma unroll
-    for (int k = 0; k < kGramStages - 1; ++k)
-        if (k < total) issue(k, k);
-    int st = 0, stn = kGramStages - 1;
-    for (int s = 0; s < total; ++s) {
-        // publish step s (this wave's copies done, later ones may stay in flight); the barrier
-        // also retires step s - 1, whose stage the copies of step s + 2 reuse
-        wait_copies<4>(min(s + kGramStages - 2, total - 1) - s);
-        __syncthreads();
-        if (s + kGramStages - 1 < total) issue(s + kGramStages - 1, stn);
-        if (active) {
-            const uint16_t* S = lds + st * (kGramStage / 2);
+        for (int q = 0; q < NQ; ++q) {
             u32x4 av[4], bv[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
-                av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * wm + mi) * 512 + 8 * lane);
+                av[mi] = *reinterpret_cast<const u32x4*>(S + (4 * wm + mi) * 1024 + lofs[q]);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-                bv[ni] = *reinterpret_cast<const u32x4*>(S + (8 + 4 * wn + ni) * 512 + 8 * lane);
-            if (s < nA) {
+                bv[ni] = *reinterpret_cast<const u32x4*>(S + (8 + 4 * wn + ni) * 1024 + lofs[q]);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) ga[mi][ni] = mfma_bf16(av[mi], bv[ni], ga[mi][ni]);
-            } else {
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) gg[mi][ni] = mfma_bf16(av[mi], bv[ni], gg[mi][ni]);
-            }
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_bf16(av[mi], bv[ni], acc[mi][ni]);
         }
-        st = st == kGramStages - 1 ? 0 : st + 1;
-        stn = stn == kGramStages - 1 ? 0 : stn + 1;
+    };
+    if (total > 0) issue(0, 0);
+    int s = 0;
+    // publish step s (this wave's copies done, the next step's may stay in flight); the barrier
+    // also retires step s - 1, whose stage the copies of step s + 1 reuse
+    auto begin = [&]() -> const uint16_t* {
+        if (s + 1 < total) {
+            __syncthreads();   // step s - 1's stage is free
+            issue(s + 1, (s + 1) & 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        return lds + (s & 1) * (kGramStage / 2);
+    };
+    // one loop per phase and kind of step, so that each loop touches one accumulator set
+    for (const int e = nA - (halfA ? 1 : 0); s < e; ++s) {
+        const uint16_t* S = begin();
+        if (active) step(S, ga, Subs<2>{});
+    }
+    if (halfA) {
+        const uint16_t* S = begin();
+        if (active) step(S, ga, Subs<1>{});
+        ++s;
+    }
+    for (const int e = total - (halfG ? 1 : 0); s < e; ++s) {
+        const uint16_t* S = begin();
+        if (active) step(S, gg, Subs<2>{});
+    }
+    if (halfG) {
+        const uint16_t* S = begin();
+        if (active) step(S, gg, Subs<1>{});
+        ++s;
     }
 
     // Hadamard sum over this wave's valid entries: lane (g, c) holds rows 4g + r, column c of
@@ -346,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_norm_gram_copy(GramArgs args) {
 //
 // Stage layout: 16-row block b at 2 KB * b, its rows 0-7 in the first KB and 8-15 in the
 // second, 128 bytes per row; logical 16-byte chunk j of row r (8 features) sits at chunk
-// j ^ rec_swz(r).  An MFMA operand read (lane 16 g + c: row c, chunk 4 q + g for the q-th 32
+// j ^ row_swz(r).  An MFMA operand read (lane 16 g + c: row c, chunk 4 q + g for the q-th 32
 // features of the step) then puts the 16 rows of each 16-lane group on 16 distinct 16-byte
 // bank slots (rows of one parity differ in r >> 1).  The copies write LDS linearly by lane,
 // so the swizzle is applied to the source chunk, inside the same 128-byte line.
@@ -356,8 +399,6 @@ constexpr int kGramRecK = 64;                    // features per step
 constexpr int kGramRecMaxLds = 144 * 1024;
 constexpr int kGramRecMaxStages = 8;
 static_assert(kGramRecMaxLds / (8 * kGramRecMaxNb * 1024) >= 2, "stages");
-
-__device__ __forceinline__ int rec_swz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 63]
 __device__ __forceinline__ void wait_vm(int n) {
@@ -379,9 +420,6 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // upper-triangle 16 x 16 tile (mi <= ni) of a 64 x 64 diagonal block -> 0..9
 __host__ __device__ constexpr int tri_tile(int mi, int ni) { return mi * 4 - mi * (mi - 1) / 2 + (ni - mi); }
-
-template <int N>
-using Subs = std::integral_constant<int, N>;
 
 __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs args, int n_stages) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds_rec[];
@@ -413,12 +451,12 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
 
     // copies: wave w issues half-blocks h = (w * per + j) mod n8, j < per; lane L fetches
     // physical chunk L % 8 of row 8 (h % 2) + L / 8 of block h / 2 (token row clamped to T - 1),
-    // i.e. logical chunk (L % 8) ^ rec_swz(row); a half step reads chunk (logical & 3) instead,
+    // i.e. logical chunk (L % 8) ^ row_swz(row); a half step reads chunk (logical & 3) instead,
     // inside the row, and those LDS chunks are never read.
     const int per = (n8 + nw - 1) / nw;     // 4 .. 8
     // Half-block h of a step holds token rows 8 h .. 8 h + 7 (rows 8 e .. 8 e + 7 of 16-row block
     // h / 2, e = h % 2); this lane copies row 8 h + lane / 8 (clamped to T - 1), logical chunk
-    // (lane % 8) ^ rec_swz(8 e + lane / 8).  A wave's j-th copy has parity e = (w per + j) % 2 (8 nb
+    // (lane % 8) ^ row_swz(8 e + lane / 8).  A wave's j-th copy has parity e = (w per + j) % 2 (8 nb
     // is even), so the lane's part of the source offset is one of two values per tensor, indexed
     // by j % 2; the rows' part, 16 h d bytes, goes into the scalar base.
     const int tlast = (int)T - 1;           // T <= 256 here
@@ -430,7 +468,7 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int par = (w * per + e) & 1;
-        jls[e] = (lane & 7) ^ rec_swz(8 * par + (lane >> 3));
+        jls[e] = (lane & 7) ^ row_swz(8 * par + (lane >> 3));
         vA[e] = (uint32_t)(lane >> 3) * (uint32_t)L.d_in * 2u + 16u * (uint32_t)jls[e];
         vG[e] = (uint32_t)(lane >> 3) * (uint32_t)L.d_out * 2u + 16u * (uint32_t)jls[e];
         hi4[e] = 16u * (uint32_t)(jls[e] & 4);   // a half step reads logical chunk j & 3
@@ -465,7 +503,7 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
     // 4 q + g, for the two 32-feature halves q of a step
     int lofs[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) lofs[q] = 512 * (c >> 3) + 64 * (c & 7) + 8 * ((4 * q + g) ^ rec_swz(c));
+    for (int q = 0; q < 2; ++q) lofs[q] = 512 * (c >> 3) + 64 * (c & 7) + 8 * ((4 * q + g) ^ row_swz(c));
 
     // The copy pipeline: one feature step per barrier, the A steps then the G steps.  At step
     // s's barrier step s is copied and step s - 1 is retired, and its stage is refilled with the

@@ -3,8 +3,10 @@
 With rows 16-byte aligned and d_in, d_out multiples of 32, records of at most 256 tokens take the
 one-workgroup-per-record kernel (off-diagonal 64-token block pairs and pairs of diagonal blocks
 as wavefronts) and longer ones the 128-token block-pair kernel; these cases put T off every block
-multiple (50, 129, 150, 200, 300: one, three and four 64-token blocks, where three leaves a
-diagonal wavefront with a single block), give 1 to 17 records, and mix layer shapes.
+multiple (50, 129, 150, 200, 257, 300, 384: one, three and four 64-token blocks, where three leaves
+a diagonal wavefront with a single block, and two or three 128-token blocks), give 1 to 17 records
+(more than 8 spread a layer's block pairs over workgroup ids of every XCD), and mix layer shapes,
+with widths that are odd multiples of 32 (a half feature step) and multiples of 64.
 Per-layer squared norms are compared with the oracle (relative 2e-3, bf16 inputs) and with the
 direct path on the same data; integer inputs small enough for exact fp32 sums are compared bit
 for bit.  Misaligned rows take the register kernel and must agree as well.
@@ -59,6 +61,8 @@ def layer_norm2(shapes, T, B, As, Gs, path, shift=False):
     (200, ((64, 96), (32, 32)), 5),
     (256, ((128, 256),), 17),
     (300, ((32, 64), (64, 32)), 2),
+    (257, ((64, 96),), 3),
+    (384, ((96, 160), (256, 64)), 9),
     (64, ((512, 512),), 1),
 ])
 def test_gram_norms_against_oracle(T, shapes, B):
