@@ -3,8 +3,9 @@
 With rows 16-byte aligned and d_in, d_out multiples of 32, records of at most 256 tokens take the
 one-workgroup-per-record kernel (off-diagonal 64-token block pairs and pairs of diagonal blocks
 as wavefronts) and longer ones the 128-token block-pair kernel; these cases put T off every block
-multiple (50, 129, 150, 200, 257, 300, 384: one, three and four 64-token blocks, where three leaves
-a diagonal wavefront with a single block, and two or three 128-token blocks), give 1 to 17 records
+multiple (5, 8, 50, 129, 150, 200, 257, 300, 384: records no longer than one 8-row copy, one, three
+and four 64-token blocks, where three leaves a diagonal wavefront with a single block, and two or
+three 128-token blocks), give 1 to 17 records
 (more than 8 spread a layer's block pairs over workgroup ids of every XCD), and mix layer shapes,
 with widths that are odd multiples of 32 (a half feature step) and multiples of 64.
 Per-layer squared norms are compared with the oracle (relative 2e-3, bf16 inputs) and with the
@@ -55,6 +56,8 @@ def layer_norm2(shapes, T, B, As, Gs, path, shift=False):
 
 @pytest.mark.parametrize("T,shapes,B", [
     (50, ((32, 64), (96, 32)), 3),
+    (5, ((32, 64), (64, 96)), 4),
+    (8, ((96, 32),), 3),
     (128, ((64, 64),), 9),
     (150, ((64, 96), (96, 32)), 4),
     (129, ((32, 64),), 3),
