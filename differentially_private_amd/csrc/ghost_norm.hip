@@ -398,7 +398,9 @@ constexpr int kGramRecWaves = 8;                 // for nb = 4
 constexpr int kGramRecK = 64;                    // features per step
 constexpr int kGramRecMaxLds = 144 * 1024;
 constexpr int kGramRecMaxStages = 8;
-static_assert(kGramRecMaxLds / (8 * kGramRecMaxNb * 1024) >= 2, "stages");
+// a pair of steps per barrier needs both copied before the previous pair's barrier retires
+// its stages: 4 stages or more (nb = 4: 4; nb = 3: 6; nb <= 2: 8)
+static_assert(kGramRecMaxLds / (8 * kGramRecMaxNb * 1024) >= 4, "stages");
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 63]
 __device__ __forceinline__ void wait_vm(int n) {
@@ -505,27 +507,41 @@ __global__ __launch_bounds__(64 * kGramRecWaves) void k_norm_gram_rec(GramArgs a
 #pragma unroll
     for (int q = 0; q < 2; ++q) lofs[q] = 512 * (c >> 3) + 64 * (c & 7) + 8 * ((4 * q + g) ^ row_swz(c));
 
-    // The copy pipeline: one feature step per barrier, the A steps then the G steps.  At step
-    // s's barrier step s is copied and step s - 1 is retired, and its stage is refilled with the
-    // next step to copy (n_stages - 1 steps ahead).  Each role runs its own copy of the loop so
-    // that its accumulators live only there; both pass the same barriers.
+    // The copy pipeline: feature steps in pairs per barrier (one at the end of a phase), the A
+    // steps then the G steps, so that the second step's LDS reads overlap the first's MFMAs and
+    // the wavefronts meet half as often (189 against 201 us per launch on workload 4 with one
+    // step per barrier).  At a group's barrier its steps are copied and every earlier step is
+    // retired, and the freed stages are refilled with the next steps to copy.  Each role runs
+    // its own copy of the loop so that its accumulators live only there; both pass the same
+    // barriers.
     const int n = n_stages;
     auto pipeline = [&](auto&& step_a, auto&& step_g) {
         int next = min(n, total);   // next step to copy
         for (int k = 0; k < next; ++k) issue(k, k);
         int s = 0;
-        auto begin = [&]() -> const uint16_t* {
-            wait_vm(per * (next - s - 1));   // step s done, later ones in flight
+        // steps s .. s + m - 1 published by one barrier, which also retires the steps before s
+        auto begin = [&](int m) {
+            wait_vm(per * (next - s - m));
             __syncthreads();
             const int lim = min(total, s + n);
             for (; next < lim; ++next) issue(next, next % n);
-            return lds_rec + (s % n) * stage_elems;
         };
+        auto S = [&](int k) { return lds_rec + (k % n) * stage_elems; };
         // one loop per phase and kind of step, so that each loop touches one accumulator set
-        for (const int e = nA - (halfA ? 1 : 0); s < e; ++s) step_a(begin(), Subs<2>{});
-        if (halfA) step_a(begin(), Subs<1>{}), ++s;
-        for (const int e = total - (halfG ? 1 : 0); s < e; ++s) step_g(begin(), Subs<2>{});
-        if (halfG) step_g(begin(), Subs<1>{}), ++s;
+        for (const int e = nA - (halfA ? 1 : 0); s + 1 < e; s += 2) {
+            begin(2);
+            step_a(S(s), Subs<2>{});
+            step_a(S(s + 1), Subs<2>{});
+        }
+        if (s < nA - (halfA ? 1 : 0)) begin(1), step_a(S(s), Subs<2>{}), ++s;
+        if (halfA) begin(1), step_a(S(s), Subs<1>{}), ++s;
+        for (const int e = total - (halfG ? 1 : 0); s + 1 < e; s += 2) {
+            begin(2);
+            step_g(S(s), Subs<2>{});
+            step_g(S(s + 1), Subs<2>{});
+        }
+        if (s < total - (halfG ? 1 : 0)) begin(1), step_g(S(s), Subs<2>{}), ++s;
+        if (halfG) begin(1), step_g(S(s), Subs<1>{}), ++s;
     };
     float* parts = args.parts + rec * args.parts_stride + L.part_off;
 
