@@ -323,6 +323,30 @@ def test_workload4_full_width_few_records_whole():
     assert e0 <= tol and e1 <= tol
 
 
+def test_workload4_full_width_long_records_whole():
+    """Workload 4's four 4096 x 4096 layers at full width with records of 512 tokens (two records):
+    the Gram norms take the 128-token block-pair kernel (T > 256), the dense clipped sum 16 k-steps
+    per record; n, c, the whole pre-noise sum and the whole noised sum against the oracle."""
+    w = datagen.workload(4).with_(B=2, logical_B=2, T=512)
+    L = w.n_layers
+    say("workload 4 layers, 2 records x 512 tokens, whole outputs")
+    As = [datagen.host_tensor(w, l, 0) for l in range(L)]
+    Gs = [datagen.host_tensor(w, l, 1) for l in range(L)]
+    from _helpers import gpu_step
+    r0 = gpu_step(w, As, Gs, DEV, flags=dp.NO_NOISE)
+    r = gpu_step(w, As, Gs, DEV, plan=r0["plan"], ws=r0["ws"])
+    assert r0["plan"].layer_info(0)[0] == dp.PATH_GRAM
+    assert r0["status"] == dp.OK and r["status"] == dp.OK
+    say("workload 4 long records oracle")
+    ref = oracle.step(As, Gs, w.C, w.sigma, 0, 0)
+    tol = TOL[BF16]
+    assert max_rel(r["n"], ref["n"]) <= tol and max_rel(r["c"], ref["c"]) <= tol
+    e0 = rel_err(flat(r0["out"]), flat(ref["S"]))
+    e1 = rel_err(flat(r["out"]), flat(ref["S_noised"]))
+    say(f"  pre-noise {e0:.2e}, noised {e1:.2e}")
+    assert e0 <= tol and e1 <= tol
+
+
 def test_workload5_virtual_step_whole_outputs():
     """Workload 5 (48 LoRA layers, 4096 logical records in 16 physical batches of 256, C = 1) as the
     benchmark runs it: dpsgd_step with NO_NOISE per physical batch (ACCUMULATE after the first),
