@@ -17,8 +17,11 @@
 
 namespace dpsgd {
 
+// MB = 1: at least 3 wavefronts per SIMD (168 registers instead of 180-184, which allowed only
+// two): the reads stream with more loads in flight (the 7B-shaped LoRA sum 46.9 -> 42.7 ms, the
+// OPT-125M-shaped one 75.5 -> 67.8 us, bitwise equal); MB = 2 would spill at that bound.
 template <int DT, int MB>
-__global__ __launch_bounds__(128) void k_sum_direct(DirectArgs args) {
+__global__ __launch_bounds__(128, MB == 1 ? 3 : 1) void k_sum_direct(DirectArgs args) {
     if (args.status && *args.status) return;
     const DirectLayer& L = args.L[blockIdx.z];
     const int w = threadIdx.x >> 6;
