@@ -631,7 +631,8 @@ def users_line(args, w, torch, dev, dp, datagen):
     in_bytes = rows * sum(di + do for di, do in w.layers) * 4          # A and G read once
     gbs = in_bytes / (norm_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": None, "kernel": "k_norm_direct (ghost_norm, direct path, segment plan)",
+            "traffic": stored_traffic(f"{w.name}_segments{n_users}", "norms", "users"),
+            "kernel": "k_norm_direct (ghost_norm, direct path, segment plan)",
             "phase": "norms", "launches_per_phase": 1, "algorithmic_bytes_per_launch": in_bytes,
             "avg_ms": norm_ms,
             "stored_gradient_blocks": {"bytes_written": n_users * w.n_params * 4,
